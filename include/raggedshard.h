@@ -1,0 +1,253 @@
+/*
+ * raggedshard.h -- C-ABI of the MI355X (gfx950) RaggedShard / Distributed
+ * Buffer shard-state library.
+ *
+ * The method is veScale-FSDP as described on the awesome-system-papers page
+ * "veScale-FSDP: Flexible and High-Performance FSDP at Scale (MLSys 2026)",
+ * section "Core method".  Each entry point below names the passage of that
+ * section that defines the operation.
+ *
+ * Conventions
+ *   - Element offsets and sizes are int64 element counts.
+ *   - One "DBuffer" is a device array of m * S_b elements per bucket b, the
+ *     buckets concatenated in bucket order (bucket b starts at base_b).
+ *     Rank r's slice of bucket b is [base_b + r*S_b, base_b + (r+1)*S_b).
+ *     On one GPU all m simulated ranks live in the same array; every device
+ *     pointer argument named d_buf / d_master / d_grad / d_qm / d_qv is the
+ *     base of such a full array and the library adds base_b + r*S_b itself.
+ *   - Absmax arrays (one fp32 per quantisation block) are indexed by global
+ *     block id: buckets in order, tensors in order, blocks in order (row
+ *     blocks top to bottom, tiles row-major over the tile grid, elements in
+ *     order).  A rank's blocks of one bucket form a contiguous id range.
+ *   - bucket = RS_ALL selects every bucket, rank = RS_ALL every rank.
+ *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Every
+ *     device call is asynchronous and stream-ordered; nothing synchronises
+ *     the host except rs_plan_upload and rs_bind_views.
+ *   - Ownership: the library owns only the host-side rs_plan.  The caller
+ *     owns every device allocation (DBuffers, absmax arrays, workspace,
+ *     views) and the stream.  The library never allocates device memory.
+ *   - Errors: every call returns an rs_status; all argument checks happen on
+ *     the host before any launch, and a failed check launches nothing.
+ *     rs_last_error() returns a thread-local message for the last non-OK
+ *     status of the calling thread.
+ *   - Device pointers must be 16-byte aligned.
+ *   - Concurrency: calls on distinct plans are independent.  Device calls on
+ *     one plan share that plan's workspace scratch and must be ordered on
+ *     one stream (or synchronised by the caller).
+ */
+#ifndef RAGGEDSHARD_H
+#define RAGGEDSHARD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct rs_plan rs_plan; /* opaque, host-owned */
+
+typedef enum {
+    RS_OK = 0,
+    RS_EINVAL = -1,    /* invalid argument (null pointer, bad spec, out-of-range index, misalignment) */
+    RS_EOVERFLOW = -2, /* a size or offset does not fit in int64 / the device tables */
+    RS_ESTATE = -3,    /* call out of order: plan not uploaded, views not bound */
+    RS_EHIP = -4,      /* a HIP runtime call or kernel launch failed */
+    RS_ENOMEM = -5     /* host allocation failed, or the workspace is too small */
+} rs_status;
+
+/* Quantisation / sharding granularity of a tensor (RaggedShard section:
+ * the atomic block may be an element, a group of rows, or a 2-D block). */
+enum { RS_ELEMENT = 0, RS_ROWS = 1, RS_TILE = 2 };
+enum { RS_F32 = 0, RS_BF16 = 1 };
+enum { RS_VIEW_F32_SRC = 0, RS_VIEW_BF16_DST = 1 };
+enum { RS_ORDER_GIVEN = 0 };
+/* How a quantisation block larger than one chunk is reduced across the
+ * workgroups that share it: two launches (per-chunk partial absmax, then
+ * the update) or one launch in which the chunks of a block meet on
+ * device-scope counters. */
+enum { RS_SPLIT_TWO_PASS = 0, RS_SPLIT_COOPERATIVE = 1 };
+
+#define RS_ALL (-1)
+
+/* One RaggedShard tensor.  Row-major shape[0..ndim) (ndim 1..4).  The
+ * tensor is viewed as [R, C] with C = shape[ndim-1] (a 1-D tensor is
+ * [d0, 1]; leading dimensions fold into R).
+ *   RS_ELEMENT: every element is its own block.
+ *   RS_ROWS:    blocks of br whole rows (the last block may be shorter).
+ *   RS_TILE:    br x bc tiles (br >= 2), row-major over the tile grid; edge
+ *               tiles are clipped.
+ * bucket: communication bucket index (buckets 0..nb-1 all non-empty). */
+typedef struct {
+    int32_t ndim;
+    int32_t gran;
+    int32_t br;
+    int32_t bc;
+    int32_t bucket;
+    int32_t reserved; /* must be 0 */
+    int64_t shape[4];
+} rs_tensor_spec;
+
+/* AdamW hyper-parameters (binary64; the library rounds the derived step
+ * scalars once to binary32).  step is t >= 1. */
+typedef struct {
+    double lr, beta1, beta2, eps, weight_decay;
+    int64_t step;
+} rs_adam_hparams;
+
+/* ------------------------------------------------------------------ plan */
+
+/* Plan a layout (page section "Grouped communication: structure-aware
+ * planning (Algorithm 1)").  For each bucket independently: the minimal
+ * per-rank size S_b (a multiple of g_coll) such that the bucket's tensors,
+ * in the given order, sit in one buffer of m*S_b elements with
+ *   - no block split across two ranks (Non-Sharded Block; a cut inside a
+ *     tensor falls on a multiple of its cut unit: 1 element, br whole rows),
+ *   - each tensor contiguous, padding only between tensors (Contiguous
+ *     Tensor Memory), every offset a multiple of lcm(g_coll, elements of one
+ *     block),
+ *   - m equal slices (Balanced Load);
+ * among placements with that S_b the lexicographically smallest offsets.
+ * Host only, synchronous.  order must be RS_ORDER_GIVEN.
+ * On success *out receives a new plan (free with rs_plan_free).
+ * Errors: RS_EINVAL (n < 1, m < 1, g_coll < 1, bad spec, empty bucket),
+ * RS_EOVERFLOW (sizes beyond 2^50 elements), RS_ENOMEM. */
+rs_status rs_plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t g_coll,
+                         int32_t order, rs_plan** out);
+
+/* Releases a plan (NULL is allowed).  Does not touch device memory. */
+void rs_plan_free(rs_plan* plan);
+
+/* Whole-plan sizes: tensor count, bucket count, ranks, total buffer
+ * elements (sum of m*S_b) and total quantisation blocks.  Any output
+ * pointer may be NULL. */
+rs_status rs_plan_info(const rs_plan* plan, int32_t* n_tensors, int32_t* n_buckets, int32_t* m,
+                       int64_t* total_elems, int64_t* n_blocks);
+
+/* Per-bucket results: S_b, base_b, padding elements (m*S_b minus real
+ * elements) and block count.  Any output pointer may be NULL. */
+rs_status rs_plan_bucket(const rs_plan* plan, int32_t bucket, int64_t* S, int64_t* base,
+                         int64_t* padding, int64_t* n_blocks);
+
+/* offsets[i] = bucket-relative offset of tensor i; blk0[i] = global id of
+ * its first block.  Arrays of n entries; either may be NULL. */
+rs_status rs_plan_offsets(const rs_plan* plan, int64_t* offsets, int64_t* blk0);
+
+/* Global block id range [first, first+count) of rank's blocks in bucket. */
+rs_status rs_plan_rank_blocks(const rs_plan* plan, int32_t bucket, int32_t rank, int64_t* first,
+                              int64_t* count);
+
+/* Maximum elements one workgroup handles in the step (a multiple of 16 in
+ * 64..16384, default 16384).  Larger blocks are split into chunks.  Must be
+ * called before rs_plan_upload.  Errors: RS_EINVAL, RS_ESTATE (uploaded). */
+rs_status rs_plan_set_chunk(rs_plan* plan, int64_t chunk_elems);
+
+/* RS_SPLIT_TWO_PASS (default) or RS_SPLIT_COOPERATIVE; may change at any
+ * time between calls. */
+rs_status rs_plan_set_split_mode(rs_plan* plan, int32_t mode);
+
+/* Number of chunks of the step's work table (valid after the chunk size is
+ * fixed; for sizing and reporting). */
+rs_status rs_plan_chunk_count(const rs_plan* plan, int64_t* n_chunks);
+
+/* Device bytes the workspace must provide (tables + scratch). */
+size_t rs_plan_device_bytes(const rs_plan* plan);
+
+/* Persistent address mapping (DBuffer section): copies the plan's tables
+ * into the caller's device workspace (>= rs_plan_device_bytes bytes,
+ * 256-byte aligned) and zeroes its scratch.  The plan keeps d_workspace;
+ * the caller keeps it alive until the plan is freed.  Synchronises the
+ * stream.  Errors: RS_EINVAL, RS_ENOMEM (bytes too small), RS_EHIP. */
+rs_status rs_plan_upload(rs_plan* plan, void* d_workspace, size_t bytes, void* stream);
+
+/* Binds per-tensor device views (DBuffer section: zero-copy per-parameter
+ * data pointers):
+ *   RS_VIEW_F32_SRC:  d_ptrs[i] -> N_i fp32 values of tensor i (pack source)
+ *   RS_VIEW_BF16_DST: d_ptrs[i] -> N_i bf16 values of tensor i (unpack
+ *                     destination; a view equal to d_buf + pos_i aliases the
+ *                     gathered buffer and is skipped by rs_unpack_full).
+ * d_ptrs is a host array of n device pointers (16-byte aligned).
+ * Synchronises the stream.  Errors: RS_EINVAL, RS_ESTATE (not uploaded). */
+rs_status rs_bind_views(rs_plan* plan, int32_t which, void* const* d_ptrs, void* stream);
+
+/* ------------------------------------------------------------ copy in/out */
+
+/* Copy-in (DBuffer section; copy is one of the fused group ops): for every
+ * position p of the selected slices, d_buf[p] = bf16_rne(view_t[p - pos_t])
+ * when p lies in tensor t, and 0 in padding.  bf16_rne: round to nearest
+ * even, NaN -> quiet NaN with its sign.  rank = RS_ALL packs all m slices
+ * (on one GPU: the all-gathered buffer).  Needs RS_VIEW_F32_SRC views.
+ * Errors: RS_EINVAL, RS_ESTATE, RS_EHIP. */
+rs_status rs_pack_shard(const rs_plan* plan, int32_t bucket, int32_t rank, uint16_t* d_buf,
+                        void* stream);
+
+/* Copy-out: view_t[i] = d_buf[pos_t + i] for every tensor of the selected
+ * bucket(s); views that alias d_buf are skipped (zero copy).  Needs
+ * RS_VIEW_BF16_DST views.  Errors: RS_EINVAL, RS_ESTATE, RS_EHIP. */
+rs_status rs_unpack_full(const rs_plan* plan, int32_t bucket, const uint16_t* d_buf,
+                         void* stream);
+
+/* -------------------------------------------------------------- group ops
+ * DBuffer section: one fused launch per op over all selected slices of a
+ * DBuffer (padding included).  dtype RS_F32 or RS_BF16. */
+
+/* d_buf[p] = +0. */
+rs_status rs_group_zero(const rs_plan* plan, int32_t bucket, int32_t rank, void* d_buf,
+                        int32_t dtype, void* stream);
+
+/* fp32: x * s;  bf16: bf16_rne(float(x) * s). */
+rs_status rs_group_scale(const rs_plan* plan, int32_t bucket, int32_t rank, void* d_buf,
+                         int32_t dtype, float s, void* stream);
+
+/* *d_sumsq = sum of float(x)^2 over the selection, squares and sum in
+ * binary64 (the global L2 norm is its square root; per-rank values are the
+ * partial sums an all-reduce would add).  Deterministic: a fixed two-level
+ * reduction order.  NaN / Inf propagate.  d_sumsq: one device double. */
+rs_status rs_group_l2norm(const rs_plan* plan, int32_t bucket, int32_t rank, const void* d_buf,
+                          int32_t dtype, double* d_sumsq, void* stream);
+
+/* Gradient-clipping coefficient on the device:
+ * *d_scale = (float) min(1, max_norm / (sqrt(*d_sumsq) + 1e-6)), in binary64. */
+rs_status rs_clip_coef(const double* d_sumsq, double max_norm, float* d_scale, void* stream);
+
+/* ----------------------------------------------------------- int8 AdamW */
+
+/* Blockwise-int8 AdamW over the selected slices (page section
+ * "Structure-aware training case study": 8-bit Adam with a per-parameter
+ * block granularity, each block quantised on its own, no metadata
+ * exchanged between blocks).  For every block B of the selection:
+ *   g  = float(d_grad[i]) * s          (s = *d_grad_scale, or 1 if NULL)
+ *   m^ = (q_m[i] / 127) * amax_m[B],   v^ = (q_v[i] / 255) * amax_v[B]
+ *   m  = b1*m^ + (1-b1)*g,             v  = b2*v^ + (1-b2)*g*g
+ *   theta = theta*(1 - lr*wd) - (lr/(1-b1^t)) * m / (sqrt(v)/sqrt(1-b2^t) + eps)
+ *   amax_m[B] = max|m|, amax_v[B] = max v,
+ *   q_m[i] = rne(m/amax_m*127) (0 if amax 0), q_v[i] = rne(v/amax_v*255).
+ * All arithmetic binary32; the quantisation codes are exact (correctly
+ * rounded division); theta may differ from a correctly rounded evaluation
+ * by a few ulp.  d_master fp32, d_grad bf16, d_qm int8, d_qv uint8 are
+ * full DBuffers; d_amax_m / d_amax_v hold one fp32 per global block.
+ * d_bf16_out (nullable): bf16_rne(theta) written at the same positions
+ * (fused copy-in).  Padding positions are never read or written.
+ * Errors: RS_EINVAL, RS_ESTATE, RS_EHIP. */
+rs_status rs_adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float* d_master,
+                        const uint16_t* d_grad, int8_t* d_qm, uint8_t* d_qv, float* d_amax_m,
+                        float* d_amax_v, const rs_adam_hparams* hp, const float* d_grad_scale,
+                        uint16_t* d_bf16_out, void* stream);
+
+/* Synchronises the stream and reports a device-side failure of the
+ * cooperative step: RS_EHIP if a bounded wait for the other chunks of a
+ * block gave up since the last check (the affected blocks then hold
+ * unspecified codes; re-upload the plan before further cooperative calls),
+ * else RS_OK.  Clears the device flag. */
+rs_status rs_plan_check_device(rs_plan* plan, void* stream);
+
+/* Thread-local message of the last non-OK status ("" if none). */
+const char* rs_last_error(void);
+
+/* Library version string. */
+const char* rs_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RAGGEDSHARD_H */

@@ -194,6 +194,13 @@ def check_plan(specs: Sequence, m: int, g_coll: int, S: int, offsets: Sequence[i
     return int(lib().orc_check_plan(_tensors(specs), n, m, g_coll, S, off))
 
 
+def block_first_position(spec, p0: int, k: int) -> int:
+    out = np.empty(1, dtype=np.int64)
+    lib().orc_block_positions(C.byref(_tensor(spec)), p0, k,
+                              out.ctypes.data_as(C.POINTER(C.c_int64)), 1)
+    return int(out[0])
+
+
 def block_positions(spec, p0: int, k: int) -> np.ndarray:
     cnt = lib().orc_block_positions(C.byref(_tensor(spec)), p0, k, None, 0)
     out = np.empty(max(cnt, 1), dtype=np.int64)
@@ -282,6 +289,9 @@ class Layout:
 
     def block_positions(self, t: int, k: int) -> np.ndarray:
         return block_positions(self.specs[t], self.pos[t], k)
+
+    def block_first_position(self, t: int, k: int) -> int:
+        return block_first_position(self.specs[t], self.pos[t], k)
 
     # -------------------------------------------------------------- ops
     def pack(self, bucket: int, rank: int, views: Sequence[np.ndarray], buf: np.ndarray):

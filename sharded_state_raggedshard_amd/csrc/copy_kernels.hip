@@ -1,0 +1,367 @@
+// DBuffer copy-in / copy-out and group ops for gfx950.
+//
+// veScale-FSDP page, section "Distributed Buffer (DBuffer)": the buffer
+// offers fused group operations (scale, zero, copy) over all tensors of a
+// bucket, and a persistent address map gives every parameter a fixed
+// location inside the buffer.  Here each op is one launch over the selected
+// slices; the copy kernels walk the planned tensor table so a tile of the
+// buffer is a handful of straight segments (tensor data or padding), moved
+// with 16-byte accesses.
+#include <hip/hip_runtime.h>
+
+#include "launch.hpp"
+#include "raggedshard.h"
+
+namespace rs {
+
+namespace {
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+    uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
+    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (data read once: non-temporal hint)
+__device__ __forceinline__ uint4 load_stream(const void* p) {
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
+}
+
+// Which range a workgroup belongs to (ranges are few; uniform scan).
+__device__ __forceinline__ int find_range(const Ranges& r, int64_t wg) {
+    int i = 0;
+    while (i + 1 < r.n && r.wg0[i + 1] <= wg) ++i;
+    return i;
+}
+
+// Tile [t0, t1) of workgroup wg under copy tiling.
+__device__ __forceinline__ void tile_of(const Ranges& r, int64_t wg, int64_t& t0, int64_t& t1) {
+    int i = find_range(r, wg);
+    int64_t tile = r.lo[i] / kCopyTile + (wg - r.wg0[i]);
+    t0 = max(r.lo[i], tile * kCopyTile);
+    t1 = min(r.hi[i], (tile + 1) * kCopyTile);
+}
+
+// ---------------------------------------------------------------- pack
+
+__device__ __forceinline__ void zero_seg16(uint16_t* buf, int64_t s, int64_t e) {
+    const int tid = threadIdx.x;
+    int64_t b0 = min(e, (s + 7) & ~int64_t(7));
+    int64_t b1 = max(b0, e & ~int64_t(7));
+    for (int64_t p = s + tid; p < b0; p += kCopyThreads) buf[p] = 0;
+    for (int64_t p = b1 + tid; p < e; p += kCopyThreads) buf[p] = 0;
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int64_t p = b0 + int64_t(tid) * 8; p < b1; p += int64_t(kCopyThreads) * 8)
+        *reinterpret_cast<uint4*>(buf + p) = z;
+}
+
+__device__ __forceinline__ void pack_seg(uint16_t* buf, const float* src, int64_t tstart, int64_t s,
+                                         int64_t e, bool vec) {
+    const int tid = threadIdx.x;
+    if (!vec) {
+        for (int64_t p = s + tid; p < e; p += kCopyThreads) buf[p] = f32_to_bf16(src[p - tstart]);
+        return;
+    }
+    int64_t b0 = min(e, (s + 7) & ~int64_t(7));
+    int64_t b1 = max(b0, e & ~int64_t(7));
+    for (int64_t p = s + tid; p < b0; p += kCopyThreads) buf[p] = f32_to_bf16(src[p - tstart]);
+    for (int64_t p = b1 + tid; p < e; p += kCopyThreads) buf[p] = f32_to_bf16(src[p - tstart]);
+    for (int64_t p = b0 + int64_t(tid) * 8; p < b1; p += int64_t(kCopyThreads) * 8) {
+        const float* sp = src + (p - tstart);
+        const uint4 x0 = load_stream(sp);
+        const uint4 x1 = load_stream(sp + 4);
+        uint4 o;
+        o.x = pack2(__uint_as_float(x0.x), __uint_as_float(x0.y));
+        o.y = pack2(__uint_as_float(x0.z), __uint_as_float(x0.w));
+        o.z = pack2(__uint_as_float(x1.x), __uint_as_float(x1.y));
+        o.w = pack2(__uint_as_float(x1.z), __uint_as_float(x1.w));
+        *reinterpret_cast<uint4*>(buf + p) = o;
+    }
+}
+
+__global__ __launch_bounds__(kCopyThreads) void pack_kernel(Ranges r, TensorTables tt,
+                                                             uint16_t* __restrict__ buf) {
+    int64_t t0, t1;
+    tile_of(r, blockIdx.x, t0, t1);
+    int j = tt.gidx[t0 / kGranule];
+    while (j < tt.n && tt.tend[j] <= t0) ++j;
+    int64_t cur = t0;
+    while (cur < t1) {
+        if (j < tt.n && tt.tstart[j] < t1) {
+            const int64_t ts = tt.tstart[j];
+            const int64_t s = max(cur, ts);
+            if (s > cur) zero_seg16(buf, cur, s);
+            const int64_t e = min(t1, tt.tend[j]);
+            pack_seg(buf, reinterpret_cast<const float*>(tt.views[j]), ts, s, e, tt.vec_ok != 0);
+            cur = e;
+            ++j;
+        } else {
+            zero_seg16(buf, cur, t1);
+            cur = t1;
+        }
+    }
+}
+
+// -------------------------------------------------------------- unpack
+
+__global__ __launch_bounds__(kCopyThreads) void unpack_kernel(Ranges r, TensorTables tt,
+                                                               const uint16_t* __restrict__ buf) {
+    int64_t t0, t1;
+    tile_of(r, blockIdx.x, t0, t1);
+    int j = tt.gidx[t0 / kGranule];
+    while (j < tt.n && tt.tend[j] <= t0) ++j;
+    const int tid = threadIdx.x;
+    for (; j < tt.n && tt.tstart[j] < t1; ++j) {
+        const int64_t ts = tt.tstart[j];
+        uint16_t* dst = reinterpret_cast<uint16_t*>(tt.views[j]);
+        if (dst == buf + ts) continue;  // the view aliases the gathered buffer
+        const int64_t s = max(t0, ts);
+        const int64_t e = min(t1, tt.tend[j]);
+        if (!tt.vec_ok) {
+            for (int64_t p = s + tid; p < e; p += kCopyThreads) dst[p - ts] = buf[p];
+            continue;
+        }
+        int64_t b0 = min(e, (s + 7) & ~int64_t(7));
+        int64_t b1 = max(b0, e & ~int64_t(7));
+        for (int64_t p = s + tid; p < b0; p += kCopyThreads) dst[p - ts] = buf[p];
+        for (int64_t p = b1 + tid; p < e; p += kCopyThreads) dst[p - ts] = buf[p];
+        for (int64_t p = b0 + int64_t(tid) * 8; p < b1; p += int64_t(kCopyThreads) * 8) {
+            uint4 v = load_stream(buf + p);
+            *reinterpret_cast<uint4*>(dst + (p - ts)) = v;
+        }
+    }
+}
+
+// ----------------------------------------------------------- group ops
+
+// Elements per 16-byte vector: 8 (bf16) or 4 (fp32).
+template <typename T>
+struct VecOf;
+template <>
+struct VecOf<uint16_t> {
+    static constexpr int n = 8;
+};
+template <>
+struct VecOf<float> {
+    static constexpr int n = 4;
+};
+
+template <typename T>
+__global__ __launch_bounds__(kCopyThreads) void zero_kernel(Ranges r, T* __restrict__ buf) {
+    constexpr int V = VecOf<T>::n;
+    int64_t t0, t1;
+    tile_of(r, blockIdx.x, t0, t1);
+    const int tid = threadIdx.x;
+    int64_t b0 = min(t1, (t0 + V - 1) & ~int64_t(V - 1));
+    int64_t b1 = max(b0, t1 & ~int64_t(V - 1));
+    for (int64_t p = t0 + tid; p < b0; p += kCopyThreads) buf[p] = T(0);
+    for (int64_t p = b1 + tid; p < t1; p += kCopyThreads) buf[p] = T(0);
+    const uint4 z = make_uint4(0, 0, 0, 0);
+    for (int64_t p = b0 + int64_t(tid) * V; p < b1; p += int64_t(kCopyThreads) * V)
+        *reinterpret_cast<uint4*>(buf + p) = z;
+}
+
+__device__ __forceinline__ float scale1(float x, float f) { return x * f; }
+__device__ __forceinline__ uint16_t scale1(uint16_t x, float f) {
+    return f32_to_bf16(bf16_to_f32(x) * f);
+}
+__device__ __forceinline__ uint4 scale_vec(uint4 v, float f, uint16_t*) {
+    uint4 o;
+    o.x = pack2(bf16_to_f32(v.x & 0xffffu) * f, bf16_to_f32(v.x >> 16) * f);
+    o.y = pack2(bf16_to_f32(v.y & 0xffffu) * f, bf16_to_f32(v.y >> 16) * f);
+    o.z = pack2(bf16_to_f32(v.z & 0xffffu) * f, bf16_to_f32(v.z >> 16) * f);
+    o.w = pack2(bf16_to_f32(v.w & 0xffffu) * f, bf16_to_f32(v.w >> 16) * f);
+    return o;
+}
+__device__ __forceinline__ uint4 scale_vec(uint4 v, float f, float*) {
+    uint4 o;
+    o.x = __float_as_uint(__uint_as_float(v.x) * f);
+    o.y = __float_as_uint(__uint_as_float(v.y) * f);
+    o.z = __float_as_uint(__uint_as_float(v.z) * f);
+    o.w = __float_as_uint(__uint_as_float(v.w) * f);
+    return o;
+}
+
+template <typename T>
+__global__ __launch_bounds__(kCopyThreads) void scale_kernel(Ranges r, T* __restrict__ buf, float f) {
+    constexpr int V = VecOf<T>::n;
+    int64_t t0, t1;
+    tile_of(r, blockIdx.x, t0, t1);
+    const int tid = threadIdx.x;
+    int64_t b0 = min(t1, (t0 + V - 1) & ~int64_t(V - 1));
+    int64_t b1 = max(b0, t1 & ~int64_t(V - 1));
+    for (int64_t p = t0 + tid; p < b0; p += kCopyThreads) buf[p] = scale1(buf[p], f);
+    for (int64_t p = b1 + tid; p < t1; p += kCopyThreads) buf[p] = scale1(buf[p], f);
+    for (int64_t p = b0 + int64_t(tid) * V; p < b1; p += int64_t(kCopyThreads) * V) {
+        uint4* q = reinterpret_cast<uint4*>(buf + p);
+        *q = scale_vec(*q, f, (T*)nullptr);
+    }
+}
+
+__device__ __forceinline__ double sq1(float x) { return (double)x * (double)x; }
+__device__ __forceinline__ double sq1(uint16_t x) {
+    double d = (double)bf16_to_f32(x);
+    return d * d;
+}
+__device__ __forceinline__ double sq_vec(uint4 v, uint16_t*) {
+    double a = 0.0;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double lo = (double)bf16_to_f32(w[i] & 0xffffu);
+        double hi = (double)bf16_to_f32(w[i] >> 16);
+        a += lo * lo;
+        a += hi * hi;
+    }
+    return a;
+}
+__device__ __forceinline__ double sq_vec(uint4 v, float*) {
+    double a = 0.0;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        double x = (double)__uint_as_float(w[i]);
+        a += x * x;
+    }
+    return a;
+}
+
+// Workgroup-wide sum in a fixed tree order; result valid in thread 0.
+__device__ __forceinline__ double wg_sum(double v) {
+    __shared__ double red[kCopyThreads / 64];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = v;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0)
+        for (int i = 0; i < kCopyThreads / 64; ++i) s += red[i];
+    return s;
+}
+
+// Fixed grid (nwg workgroups); workgroup w takes tiles w, w + nwg, ...
+template <typename T>
+__global__ __launch_bounds__(kCopyThreads) void sumsq_partial_kernel(Ranges r, const T* __restrict__ buf,
+                                                                     int64_t ntiles, double* part) {
+    constexpr int V = VecOf<T>::n;
+    const int tid = threadIdx.x;
+    double acc = 0.0;
+    for (int64_t wg = blockIdx.x; wg < ntiles; wg += gridDim.x) {
+        int64_t t0, t1;
+        tile_of(r, wg, t0, t1);
+        int64_t b0 = min(t1, (t0 + V - 1) & ~int64_t(V - 1));
+        int64_t b1 = max(b0, t1 & ~int64_t(V - 1));
+        for (int64_t p = t0 + tid; p < b0; p += kCopyThreads) acc += sq1(buf[p]);
+        for (int64_t p = b1 + tid; p < t1; p += kCopyThreads) acc += sq1(buf[p]);
+        for (int64_t p = b0 + int64_t(tid) * V; p < b1; p += int64_t(kCopyThreads) * V)
+            acc += sq_vec(load_stream(buf + p), (T*)nullptr);
+    }
+    double s = wg_sum(acc);
+    if (tid == 0) part[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(kCopyThreads) void sumsq_final_kernel(const double* part, int n,
+                                                                   double* out) {
+    double acc = 0.0;
+    for (int i = threadIdx.x; i < n; i += kCopyThreads) acc += part[i];
+    double s = wg_sum(acc);
+    if (threadIdx.x == 0) *out = s;
+}
+
+__global__ void clip_kernel(const double* sumsq, double max_norm, float* scale) {
+    if (threadIdx.x == 0 && blockIdx.x == 0) {
+        double c = max_norm / (sqrt(*sumsq) + 1e-6);
+        if (c > 1.0) c = 1.0;
+        *scale = (float)c;
+    }
+}
+
+}  // namespace
+
+int64_t tile_ranges(Ranges& r) {
+    int64_t total = 0;
+    for (int i = 0; i < r.n; ++i) {
+        r.wg0[i] = total;
+        if (r.hi[i] > r.lo[i]) total += (r.hi[i] - 1) / kCopyTile - r.lo[i] / kCopyTile + 1;
+    }
+    r.wg0[r.n] = total;
+    return total;
+}
+
+hipError_t launch_pack(const Ranges& r, const TensorTables& tt, uint16_t* buf, hipStream_t s) {
+    Ranges rr = r;
+    int64_t nwg = tile_ranges(rr);
+    if (nwg == 0) return hipSuccess;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)nwg), dim3(kCopyThreads), 0, s, rr, tt, buf);
+    return hipGetLastError();
+}
+
+hipError_t launch_unpack(const Ranges& r, const TensorTables& tt, const uint16_t* buf,
+                         hipStream_t s) {
+    Ranges rr = r;
+    int64_t nwg = tile_ranges(rr);
+    if (nwg == 0) return hipSuccess;
+    hipLaunchKernelGGL(unpack_kernel, dim3((unsigned)nwg), dim3(kCopyThreads), 0, s, rr, tt, buf);
+    return hipGetLastError();
+}
+
+hipError_t launch_zero(const Ranges& r, void* buf, int32_t dtype, hipStream_t s) {
+    Ranges rr = r;
+    int64_t nwg = tile_ranges(rr);
+    if (nwg == 0) return hipSuccess;
+    if (dtype == RS_BF16)
+        hipLaunchKernelGGL(zero_kernel<uint16_t>, dim3((unsigned)nwg), dim3(kCopyThreads), 0, s,
+                           rr, (uint16_t*)buf);
+    else
+        hipLaunchKernelGGL(zero_kernel<float>, dim3((unsigned)nwg), dim3(kCopyThreads), 0, s, rr,
+                           (float*)buf);
+    return hipGetLastError();
+}
+
+hipError_t launch_scale(const Ranges& r, void* buf, int32_t dtype, float f, hipStream_t s) {
+    Ranges rr = r;
+    int64_t nwg = tile_ranges(rr);
+    if (nwg == 0) return hipSuccess;
+    if (dtype == RS_BF16)
+        hipLaunchKernelGGL(scale_kernel<uint16_t>, dim3((unsigned)nwg), dim3(kCopyThreads), 0, s,
+                           rr, (uint16_t*)buf, f);
+    else
+        hipLaunchKernelGGL(scale_kernel<float>, dim3((unsigned)nwg), dim3(kCopyThreads), 0, s, rr,
+                           (float*)buf, f);
+    return hipGetLastError();
+}
+
+hipError_t launch_l2norm(const Ranges& r, const void* buf, int32_t dtype, double* d_partials,
+                         double* d_out, hipStream_t s) {
+    Ranges rr = r;
+    int64_t ntiles = tile_ranges(rr);
+    int nwg = (int)std::min<int64_t>(std::max<int64_t>(ntiles, 1), kL2Blocks);
+    if (dtype == RS_BF16)
+        hipLaunchKernelGGL(sumsq_partial_kernel<uint16_t>, dim3(nwg), dim3(kCopyThreads), 0, s,
+                           rr, (const uint16_t*)buf, ntiles, d_partials);
+    else
+        hipLaunchKernelGGL(sumsq_partial_kernel<float>, dim3(nwg), dim3(kCopyThreads), 0, s, rr,
+                           (const float*)buf, ntiles, d_partials);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(sumsq_final_kernel, dim3(1), dim3(kCopyThreads), 0, s, d_partials, nwg,
+                       d_out);
+    return hipGetLastError();
+}
+
+hipError_t launch_clip(const double* d_sumsq, double max_norm, float* d_scale, hipStream_t s) {
+    hipLaunchKernelGGL(clip_kernel, dim3(1), dim3(64), 0, s, d_sumsq, max_norm, d_scale);
+    return hipGetLastError();
+}
+
+}  // namespace rs

@@ -1,0 +1,74 @@
+// Kernel launchers (implemented in the .hip files).  Plain pointers only.
+#pragma once
+#include <hip/hip_runtime_api.h>
+
+#include <cstdint>
+
+#include "tables.hpp"
+
+namespace rs {
+
+constexpr int kMaxRanges = 64;
+
+// Up to kMaxRanges half-open element ranges [lo, hi) of one launch, with the
+// prefix count of workgroups assigned to each.
+struct Ranges {
+    int32_t n;
+    int32_t pad;
+    int64_t lo[kMaxRanges];
+    int64_t hi[kMaxRanges];
+    int64_t wg0[kMaxRanges + 1];
+};
+
+// Copy kernels work on tiles of kCopyTile elements aligned to absolute
+// multiples of kCopyTile (a divisor of kGranule).
+constexpr int64_t kCopyTile = 8192;
+constexpr int kCopyThreads = 256;
+
+// Tensor tables in buffer order (device).
+struct TensorTables {
+    const int64_t* tstart;
+    const int64_t* tend;
+    const uint64_t* views;  // fp32 sources (pack) or bf16 destinations (unpack)
+    const int32_t* gidx;
+    int32_t n;
+    int32_t vec_ok;  // every start % 8 == 0 and every view 16-byte aligned
+};
+
+// Fills wg0 for copy-style tiling; returns the total workgroup count.
+int64_t tile_ranges(Ranges& r);
+
+hipError_t launch_pack(const Ranges& r, const TensorTables& tt, uint16_t* buf, hipStream_t s);
+hipError_t launch_unpack(const Ranges& r, const TensorTables& tt, const uint16_t* buf,
+                         hipStream_t s);
+hipError_t launch_zero(const Ranges& r, void* buf, int32_t dtype, hipStream_t s);
+hipError_t launch_scale(const Ranges& r, void* buf, int32_t dtype, float f, hipStream_t s);
+hipError_t launch_l2norm(const Ranges& r, const void* buf, int32_t dtype, double* d_partials,
+                         double* d_out, hipStream_t s);
+hipError_t launch_clip(const double* d_sumsq, double max_norm, float* d_scale, hipStream_t s);
+
+// fp32 step scalars derived on the host.
+struct StepScalars {
+    float beta1, beta2, omega1, omega2, eps, c_decay, step_size, kappa;
+};
+
+struct StepBuffers {
+    float* theta;
+    const uint16_t* grad;
+    int8_t* qm;
+    uint8_t* qv;
+    float* amax_m;
+    float* amax_v;
+    const float* gscale;  // nullable
+    uint16_t* out;        // nullable
+    const ChunkDesc* chunks;
+    ChunkPartial* cpart;
+    CoopSlot* coop;
+    CoopCounters* counters;
+};
+
+// Chunk-index ranges [lo, hi) of the chunk table; mode RS_SPLIT_*.
+hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const StepScalars& sc,
+                        int32_t mode, hipStream_t s);
+
+}  // namespace rs

@@ -1,0 +1,542 @@
+// RaggedShard layout planner and device work-table builder (host C++).
+//
+// Layout problem: veScale-FSDP page, section "Grouped communication:
+// structure-aware planning (Algorithm 1)".  Given the tensors of a bucket in
+// their default order, find the smallest per-rank size S (a multiple of
+// g_coll) admitting a placement with no block cut by a rank boundary, each
+// tensor contiguous with padding only between tensors, offsets aligned to
+// lcm(g_coll, block elements), inside m equal slices.
+//
+// For a fixed S the admissible offsets of a tensor depend only on where the
+// previous tensor ends, and an earlier end never removes an admissible
+// offset, so earliest-offset placement is exact for that S (the page's
+// monotone dp(t, i) for a fixed order).  Feasibility is not monotone in S,
+// so S is scanned upward; two devices keep the scan short:
+//   - a tensor longer than 2S always holds two consecutive rank boundaries,
+//     so S must be a multiple of its cut unit: the scan jumps to the next
+//     such S until a tensor stops being that long;
+//   - inside one S, the earliest offset jumps straight to the next offset
+//     that repairs the first offending boundary (Chinese remaindering of the
+//     alignment and the cut unit) instead of stepping by the alignment.
+#include "plan.hpp"
+
+#include <algorithm>
+#include <limits>
+
+namespace rs {
+
+namespace {
+
+constexpr int64_t kMaxElems = int64_t(1) << 50;
+constexpr int64_t kInf = std::numeric_limits<int64_t>::max() / 4;
+
+int64_t gcd64(int64_t a, int64_t b) {
+    while (b) {
+        int64_t r = a % b;
+        a = b;
+        b = r;
+    }
+    return a;
+}
+
+// lcm, saturating at kInf
+int64_t lcm_sat(int64_t a, int64_t b) {
+    __int128 l = (__int128)(a / gcd64(a, b)) * b;
+    return l > kInf ? kInf : (int64_t)l;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+
+// modular inverse of a mod n (gcd(a, n) == 1, n > 1)
+int64_t mod_inverse(int64_t a, int64_t n) {
+    __int128 t = 0, nt = 1, r = n, nr = a % n;
+    while (nr != 0) {
+        __int128 q = r / nr;
+        __int128 tmp = t - q * nt;
+        t = nt;
+        nt = tmp;
+        tmp = r - q * nr;
+        r = nr;
+        nr = tmp;
+    }
+    if (t < 0) t += n;
+    return (int64_t)t;
+}
+
+rs_status derive(const rs_tensor_spec& s, int64_t g_coll, TensorInfo& t, std::string& err) {
+    if (s.ndim < 1 || s.ndim > 4) {
+        err = "ndim must be 1..4";
+        return RS_EINVAL;
+    }
+    if (s.reserved != 0 || s.bucket < 0) {
+        err = "bad bucket / reserved field";
+        return RS_EINVAL;
+    }
+    int64_t N = 1;
+    for (int i = 0; i < s.ndim; ++i) {
+        if (s.shape[i] < 1) {
+            err = "shape dimensions must be >= 1";
+            return RS_EINVAL;
+        }
+        if ((__int128)N * s.shape[i] > kMaxElems) {
+            err = "tensor larger than 2^50 elements";
+            return RS_EOVERFLOW;
+        }
+        N *= s.shape[i];
+    }
+    t.N = N;
+    t.C = s.ndim >= 2 ? s.shape[s.ndim - 1] : 1;
+    t.R = N / t.C;
+    t.gran = s.gran;
+    t.br = s.br;
+    t.bc = s.bc;
+    t.bucket = s.bucket;
+    switch (s.gran) {
+    case RS_ELEMENT:
+        t.u = 1;
+        t.b = 1;
+        t.nblk = N;
+        break;
+    case RS_ROWS:
+        if (s.br < 1) {
+            err = "ROWS granularity needs br >= 1";
+            return RS_EINVAL;
+        }
+        t.u = (int64_t)s.br * t.C;
+        t.b = std::min<int64_t>(s.br, t.R) * t.C;
+        t.nblk = ceil_div(t.R, s.br);
+        break;
+    case RS_TILE:
+        if (s.br < 2 || s.bc < 1) {
+            err = "TILE granularity needs br >= 2 and bc >= 1";
+            return RS_EINVAL;
+        }
+        if (t.C > (int64_t(1) << 31) - 1) {
+            err = "TILE rows wider than 2^31 elements";
+            return RS_EOVERFLOW;
+        }
+        t.u = (int64_t)s.br * t.C;
+        t.b = std::min<int64_t>(s.br, t.R) * std::min<int64_t>(s.bc, t.C);
+        t.nblk = ceil_div(t.R, s.br) * ceil_div(t.C, s.bc);
+        break;
+    default:
+        err = "unknown granularity";
+        return RS_EINVAL;
+    }
+    if (t.u > kMaxElems) {
+        err = "cut unit larger than 2^50 elements";
+        return RS_EOVERFLOW;
+    }
+    if (t.b > (int64_t(1) << 31) - 1) {
+        err = "a quantisation block holds more than 2^31 elements";
+        return RS_EOVERFLOW;
+    }
+    t.A = lcm_sat(g_coll, t.b);
+    if (t.A > kMaxElems) {
+        err = "alignment lcm(g_coll, block) larger than 2^50";
+        return RS_EOVERFLOW;
+    }
+    return RS_OK;
+}
+
+// Smallest x > o with x = 0 (mod A), x = cut (mod u), x < cut; kInf if none.
+int64_t next_aligned_cut_match(const TensorInfo& t, int64_t o, int64_t cut) {
+    int64_t g = gcd64(t.A, t.u);
+    int64_t c = cut % t.u;
+    if (c % g != 0) return kInf;
+    int64_t M = t.u / g;
+    int64_t k0 = 0;
+    if (M > 1) {
+        int64_t a = (t.A / g) % M;
+        k0 = (int64_t)(((__int128)((c / g) % M) * mod_inverse(a, M)) % M);
+    }
+    __int128 L = (__int128)t.A * M;
+    __int128 x0 = (__int128)t.A * k0;
+    __int128 x;
+    if (x0 > o)
+        x = x0;
+    else
+        x = x0 + ((((__int128)o + 1 - x0) + L - 1) / L) * L;
+    if (x >= cut) return kInf;
+    return (int64_t)x;
+}
+
+}  // namespace
+
+int64_t earliest_offset(const TensorInfo& t, int32_t m, int64_t S, int64_t e) {
+    const int64_t cap = (int64_t)m * S;
+    int64_t o = round_up(e, t.A);
+    for (;;) {
+        if (o + t.N > cap) return -1;
+        int64_t j0 = o / S + 1;
+        int64_t j1 = std::min<int64_t>(m - 1, (o + t.N - 1) / S);
+        int64_t bad = -1;
+        for (int64_t j = j0; j <= j1; ++j) {
+            if ((j * S - o) % t.u != 0) {
+                bad = j;
+                break;
+            }
+        }
+        if (bad < 0) return o;
+        int64_t cut = bad * S;
+        int64_t past = round_up(cut, t.A);
+        int64_t match = next_aligned_cut_match(t, o, cut);
+        o = std::min(past, match);
+    }
+}
+
+namespace {
+
+bool place_all(const std::vector<TensorInfo*>& ts, int32_t m, int64_t S, std::vector<int64_t>& off) {
+    int64_t e = 0;
+    for (size_t i = 0; i < ts.size(); ++i) {
+        int64_t o = earliest_offset(*ts[i], m, S, e);
+        if (o < 0) return false;
+        off[i] = o;
+        e = o + ts[i]->N;
+    }
+    return true;
+}
+
+rs_status plan_one_bucket(std::vector<TensorInfo*>& ts, int32_t m, int64_t g, int64_t& S_out,
+                          std::string& err) {
+    int64_t end0 = 0;
+    for (auto* t : ts) end0 = round_up(end0, t->A) + t->N;
+    // Every placement ends at or after end0 (the cut-free earliest
+    // placement), so m*S >= end0; this bound also covers ceil(total / m).
+    const int64_t S_lo = round_up(ceil_div(end0, m), g);
+    const int64_t S_hi = round_up(end0, g);  // everything inside rank 0: always feasible
+    std::vector<int64_t> off(ts.size());
+    int64_t S = S_lo;
+    while (S <= S_hi) {
+        int64_t L = g;
+        int64_t change = kInf;
+        for (auto* t : ts) {
+            if (t->N > 2 * S) {
+                L = lcm_sat(L, t->u);
+                change = std::min(change, ceil_div(t->N, 2));
+            }
+        }
+        if (S % L != 0) {
+            int64_t nxt = (L >= kInf) ? kInf : round_up(S, L);
+            if (change < kInf) nxt = std::min(nxt, round_up(change, g));
+            if (nxt <= S) nxt = S + g;
+            S = nxt;
+            continue;
+        }
+        if (place_all(ts, m, S, off)) {
+            for (size_t i = 0; i < ts.size(); ++i) ts[i]->off = off[i];
+            S_out = S;
+            return RS_OK;
+        }
+        S += g;
+    }
+    err = "internal: planner scan ended without a placement";
+    return RS_EINVAL;
+}
+
+// First block (global id) whose first element is at or after position P,
+// scanning the bucket's tensors in buffer order.
+int64_t first_block_at(const Plan& p, const BucketInfo& B, int64_t P) {
+    for (int32_t i : B.tensors) {
+        const TensorInfo& t = p.t[i];
+        if (t.pos + t.N <= P) continue;
+        int64_t k;
+        if (P <= t.pos) {
+            k = 0;
+        } else if (t.gran == RS_ELEMENT) {
+            k = P - t.pos;
+        } else {
+            int64_t band = ceil_div(P - t.pos, t.u);
+            k = (t.gran == RS_TILE) ? band * ceil_div(t.C, t.bc) : band;
+        }
+        if (k < t.nblk) return t.blk0 + k;
+    }
+    return B.blk0 + B.nblk;
+}
+
+}  // namespace
+
+rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t g_coll, Plan& p,
+                      std::string& err) {
+    if (!specs || n < 1 || m < 1 || g_coll < 1) {
+        err = "need specs != NULL, n >= 1, m >= 1, g_coll >= 1";
+        return RS_EINVAL;
+    }
+    if (m > (1 << 20) || g_coll > kMaxElems) {
+        err = "m or g_coll out of range";
+        return RS_EINVAL;
+    }
+    p.m = m;
+    p.g_coll = g_coll;
+    p.t.assign(n, TensorInfo{});
+    int32_t nb = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        rs_status st = derive(specs[i], g_coll, p.t[i], err);
+        if (st != RS_OK) {
+            err = "tensor " + std::to_string(i) + ": " + err;
+            return st;
+        }
+        nb = std::max(nb, specs[i].bucket + 1);
+    }
+    p.b.assign(nb, BucketInfo{});
+    for (int32_t i = 0; i < n; ++i) p.b[p.t[i].bucket].tensors.push_back(i);
+    int64_t base = 0, blk = 0;
+    p.by_pos.clear();
+    for (int32_t k = 0; k < nb; ++k) {
+        BucketInfo& B = p.b[k];
+        if (B.tensors.empty()) {
+            err = "bucket " + std::to_string(k) + " is empty";
+            return RS_EINVAL;
+        }
+        std::vector<TensorInfo*> ts;
+        for (int32_t i : B.tensors) ts.push_back(&p.t[i]);
+        rs_status st = plan_one_bucket(ts, m, g_coll, B.S, err);
+        if (st != RS_OK) return st;
+        if ((__int128)B.S * m + base > kMaxElems * 8) {
+            err = "buffer larger than 2^53 elements";
+            return RS_EOVERFLOW;
+        }
+        B.base = base;
+        B.blk0 = blk;
+        B.real = 0;
+        for (int32_t i : B.tensors) {
+            TensorInfo& t = p.t[i];
+            t.pos = base + t.off;
+            t.blk0 = blk;
+            blk += t.nblk;
+            B.real += t.N;
+            p.by_pos.push_back(i);
+        }
+        B.nblk = blk - B.blk0;
+        B.padding = (int64_t)m * B.S - B.real;
+        base += (int64_t)m * B.S;
+    }
+    p.total = base;
+    p.nblocks = blk;
+    p.rank_blk.assign(size_t(nb) * (m + 1), 0);
+    for (int32_t k = 0; k < nb; ++k) {
+        const BucketInfo& B = p.b[k];
+        for (int32_t r = 0; r <= m; ++r)
+            p.rank_blk[size_t(k) * (m + 1) + r] =
+                (r == m) ? B.blk0 + B.nblk : first_block_at(p, B, B.base + (int64_t)r * B.S);
+    }
+    p.tables_built = false;
+    return RS_OK;
+}
+
+// ------------------------------------------------------------ work tables
+
+namespace {
+
+bool pow2(int64_t x) { return x > 0 && (x & (x - 1)) == 0; }
+
+int ilog2(int64_t x) {
+    int l = 0;
+    while ((int64_t(1) << l) < x) ++l;
+    return l;
+}
+
+struct ChunkBuilder {
+    Plan& p;
+    const BucketInfo& B;
+    int64_t CH;
+    std::vector<ChunkDesc>& out;
+
+    int32_t rank_of(int64_t pos) const { return (int32_t)((pos - B.base) / B.S); }
+
+    void scalar(int64_t pos, int64_t blk, int64_t rows, int64_t cols, int64_t ld) {
+        ChunkDesc c{};
+        c.pos = pos;
+        c.blk = blk;
+        c.ld = ld;
+        c.rows = (int32_t)rows;
+        c.cols = (int32_t)cols;
+        c.part = 0;
+        c.nparts = 1;
+        c.kind = KIND_SCALAR;
+        c.vpb_log2 = -1;
+        out.push_back(c);
+    }
+
+    void vec(int64_t pos, int64_t blk, int64_t rows, int64_t cols, int64_t ld, int32_t part,
+             int32_t nparts, int32_t vpb_log2) {
+        ChunkDesc c{};
+        c.pos = pos;
+        c.blk = blk;
+        c.ld = ld;
+        c.rows = (int32_t)rows;
+        c.cols = (int32_t)cols;
+        c.part = part;
+        c.nparts = nparts;
+        c.kind = KIND_VEC;
+        c.vpb_log2 = vpb_log2;
+        out.push_back(c);
+    }
+
+    // One contiguous block [s, s + n).
+    void contiguous_block(int64_t s, int64_t n, int64_t blk) {
+        if (s % kVec != 0 || n % kVec != 0) {
+            scalar(s, blk, 1, n, n);
+            return;
+        }
+        if (n <= CH) {
+            vec(s, blk, 1, n, n, 0, 1, -1);
+            return;
+        }
+        int32_t np = (int32_t)ceil_div(n, CH);
+        for (int32_t q = 0; q < np; ++q)
+            vec(s + q * CH, blk, 1, std::min(CH, n - q * CH), 0, q, np, -1);
+    }
+
+    void tensor(const TensorInfo& t) {
+        if (t.gran == RS_ELEMENT) {
+            // runs of single-element blocks, never across a rank boundary
+            int64_t i = 0;
+            while (i < t.N) {
+                int64_t p0 = t.pos + i;
+                int64_t rank_end = B.base + (rank_of(p0) + 1) * B.S;
+                int64_t len = std::min({CH, t.N - i, rank_end - p0});
+                ChunkDesc c{};
+                c.pos = p0;
+                c.blk = t.blk0 + i;
+                c.ld = 0;
+                c.rows = 1;
+                c.cols = (int32_t)len;
+                c.part = 0;
+                c.nparts = 1;
+                c.kind = KIND_ELEM;
+                c.vpb_log2 = -1;
+                out.push_back(c);
+                i += len;
+            }
+            return;
+        }
+        const bool contiguous_blocks = (t.gran == RS_ROWS) || (t.bc >= t.C);
+        if (contiguous_blocks) {
+            // block k covers rows [k*br, min((k+1)*br, R)) in full
+            const int64_t full = t.u;  // elements of a full block
+            int64_t k = 0;
+            while (k < t.nblk) {
+                int64_t s = t.pos + k * t.u;
+                int64_t n = std::min(t.u, t.N - k * t.u);
+                int64_t vpb = n / kVec;
+                if (n == full && n % kVec == 0 && s % kVec == 0 && pow2(vpb) && vpb <= 64 &&
+                    n < CH) {
+                    // run of whole small blocks of one rank, handled by lane groups
+                    int32_t r = rank_of(s);
+                    int64_t k1 = k + 1;
+                    while (k1 < t.nblk && (k1 - k + 1) * n <= CH) {
+                        int64_t s1 = t.pos + k1 * t.u;
+                        if (std::min(t.u, t.N - k1 * t.u) != n || rank_of(s1) != r) break;
+                        ++k1;
+                    }
+                    vec(s, t.blk0 + k, 1, (k1 - k) * n, 0, 0, 1, ilog2(vpb));
+                    k = k1;
+                    continue;
+                }
+                contiguous_block(s, n, t.blk0 + k);
+                ++k;
+            }
+            return;
+        }
+        // 2-D tiles narrower than a row: rows of bc elements with stride C
+        const int64_t nbc = ceil_div(t.C, t.bc);
+        for (int64_t k = 0; k < t.nblk; ++k) {
+            int64_t bi = k / nbc, bj = k % nbc;
+            int64_t r0 = bi * t.br, rows = std::min<int64_t>(t.br, t.R - r0);
+            int64_t c0 = bj * t.bc, cols = std::min<int64_t>(t.bc, t.C - c0);
+            int64_t s = t.pos + r0 * t.C + c0;
+            if (s % kVec != 0 || cols % kVec != 0 || t.C % kVec != 0 || cols > CH) {
+                scalar(s, t.blk0 + k, rows, cols, t.C);
+                continue;
+            }
+            if (rows * cols <= CH) {
+                vec(s, t.blk0 + k, rows, cols, t.C, 0, 1, -1);
+                continue;
+            }
+            int64_t rpp = CH / cols;
+            int32_t np = (int32_t)ceil_div(rows, rpp);
+            for (int32_t q = 0; q < np; ++q)
+                vec(s + q * rpp * t.C, t.blk0 + k, std::min(rpp, rows - q * rpp), cols, t.C, q,
+                    np, -1);
+        }
+    }
+};
+
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+rs_status build_tables(Plan& p, std::string& err) {
+    const int32_t nb = (int32_t)p.b.size();
+    const int32_t m = p.m;
+    p.chunks.clear();
+    p.chunk_begin.assign(size_t(nb) * (m + 1), 0);
+    for (int32_t k = 0; k < nb; ++k) {
+        const BucketInfo& B = p.b[k];
+        size_t first = p.chunks.size();
+        ChunkBuilder cbld{p, B, p.chunk_elems, p.chunks};
+        for (int32_t i : B.tensors) cbld.tensor(p.t[i]);
+        // chunks come out in buffer order, so their ranks never decrease
+        size_t c = first;
+        for (int32_t r = 0; r <= m; ++r) {
+            int64_t lim = B.base + (int64_t)r * B.S;
+            while (c < p.chunks.size() && p.chunks[c].pos < lim) ++c;
+            p.chunk_begin[size_t(k) * (m + 1) + r] = (int64_t)c;
+        }
+        p.chunk_begin[size_t(k) * (m + 1) + m] = (int64_t)p.chunks.size();
+    }
+    for (const ChunkDesc& c : p.chunks) {
+        if (c.nparts > 65535) {
+            err = "a block needs more than 65535 chunks; raise the chunk size";
+            return RS_EOVERFLOW;
+        }
+    }
+    // tensor tables in buffer order and the granule index
+    const size_t n = p.t.size();
+    p.tstart.resize(n);
+    p.tend.resize(n);
+    for (size_t j = 0; j < n; ++j) {
+        const TensorInfo& t = p.t[p.by_pos[j]];
+        p.tstart[j] = t.pos;
+        p.tend[j] = t.pos + t.N;
+    }
+    const int64_t ngran = ceil_div(std::max<int64_t>(p.total, 1), kGranule);
+    p.gidx.assign(size_t(ngran), (int32_t)n);
+    {
+        size_t j = 0;
+        for (int64_t g = 0; g < ngran; ++g) {
+            int64_t gs = g * kGranule;
+            while (j < n && p.tend[j] <= gs) ++j;
+            p.gidx[size_t(g)] = (int32_t)j;
+        }
+    }
+    size_t off = 0;
+    p.off_tstart = off;
+    off = align256(off + n * 8);
+    p.off_tend = off;
+    off = align256(off + n * 8);
+    p.off_src = off;
+    off = align256(off + n * 8);
+    p.off_dst = off;
+    off = align256(off + n * 8);
+    p.off_gidx = off;
+    off = align256(off + size_t(ngran) * 4);
+    p.off_chunks = off;
+    off = align256(off + p.chunks.size() * sizeof(ChunkDesc));
+    p.off_cpart = off;
+    off = align256(off + p.chunks.size() * sizeof(ChunkPartial));
+    p.off_coop = off;
+    off = align256(off + p.chunks.size() * sizeof(CoopSlot));
+    p.off_l2 = off;
+    off = align256(off + size_t(kL2Blocks) * 8);
+    p.off_flag = off;
+    off = align256(off + 16);
+    p.ws_bytes = off;
+    p.tables_built = true;
+    return RS_OK;
+}
+
+}  // namespace rs

@@ -1,0 +1,202 @@
+"""Host-side checks of the C-ABI library (no GPU): symbol exports, the
+product planner against the oracle, and argument validation."""
+import ctypes as C
+import os
+import re
+import time
+
+import numpy as np
+import pytest
+
+import oracle
+import sharded_state_raggedshard_amd as rs
+import synth
+from synth import ELEMENT, ROWS, TILE, TensorSpec
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def header_functions():
+    txt = open(os.path.join(ROOT, "include", "raggedshard.h")).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(rs_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = header_functions()
+    assert len(names) >= 20
+    L = rs.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(rs.EXPORTS) == names
+    # and the shared object's dynamic symbol table has them as functions
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", rs.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    syms = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    assert set(names) <= syms
+
+
+def _oracle_rank_blocks(L, bucket):
+    """rank -> (first global block id, count) from the oracle layout: a block
+    belongs to the rank holding its first element."""
+    ids = {}
+    for i, s in enumerate(L.specs):
+        if s.bucket != bucket:
+            continue
+        for k in range(L.derived[i].nblk):
+            ids.setdefault(L.rank_of(L.block_first_position(i, k)), []).append(L.blk0[i] + k)
+    out = {}
+    for r, v in ids.items():
+        assert v == list(range(v[0], v[0] + len(v)))
+        out[r] = (v[0], len(v))
+    return out
+
+
+def _compare_plan(specs, m, g):
+    h = rs.rs_plan_layout(specs, m, g)
+    try:
+        L = oracle.Layout(specs, m, g)
+        n, nb, mm, total, nblk = rs.rs_plan_info(h)
+        assert (n, nb, mm, total, nblk) == (len(specs), L.nb, m, L.total, L.n_blocks)
+        off, blk0 = rs.rs_plan_offsets(h)
+        assert off == L.offsets and blk0 == L.blk0
+        for b in range(nb):
+            S, base, pad, nbb = rs.rs_plan_bucket(h, b)
+            assert (S, base, pad) == (L.S[b], L.base[b], L.padding(b))
+        return h, L
+    except Exception:
+        rs.rs_plan_free(h)
+        raise
+
+
+@pytest.mark.parametrize("g_coll", [1, 2, 4, 16])
+def test_product_planner_matches_oracle_on_random_tiny(g_coll):
+    rng = np.random.default_rng(77 + g_coll)
+    for _ in range(500):
+        specs = synth.random_tiny_specs(rng)
+        m = int(rng.integers(1, 5))
+        h, L = _compare_plan(specs, m, g_coll)
+        exp = _oracle_rank_blocks(L, 0)
+        for r in range(m):
+            a, c = rs.rs_plan_rank_blocks(h, 0, r)
+            if r not in exp:
+                assert c == 0
+            else:
+                assert (a, c) == exp[r]
+        rs.rs_plan_free(h)
+
+
+def test_product_planner_matches_oracle_on_mid_sizes():
+    # wider tensors, more ranks, several buckets
+    rng = np.random.default_rng(5)
+    for _ in range(150):
+        specs = []
+        for b in range(int(rng.integers(1, 4))):
+            for i in range(int(rng.integers(1, 6))):
+                kind = int(rng.integers(0, 3))
+                C_ = int(rng.choice([1, 3, 16, 32, 48]))
+                R = int(rng.integers(1, 300))
+                if kind == ELEMENT:
+                    specs.append(TensorSpec(f"e{b}{i}", (R * C_,), ELEMENT, bucket=b))
+                elif kind == ROWS:
+                    specs.append(TensorSpec(f"r{b}{i}", (R, C_), ROWS, int(rng.integers(1, 40)),
+                                            bucket=b))
+                else:
+                    specs.append(TensorSpec(f"t{b}{i}", (max(R, 2), C_), TILE,
+                                            int(rng.integers(2, 40)), int(rng.integers(1, 40)),
+                                            bucket=b))
+        m = int(rng.integers(1, 17))
+        g = int(rng.choice([1, 4, 16, 64]))
+        h, L = _compare_plan(specs, m, g)
+        rs.rs_plan_free(h)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama_layer", "llama8b_tiles", "moe", "llama8b_full"])
+def test_product_planner_matches_oracle_on_workloads(name):
+    w = synth.WORKLOADS[name]()
+    t0 = time.perf_counter()
+    h = rs.rs_plan_layout(w.specs, w.m, w.g_coll)
+    dt = time.perf_counter() - t0
+    # one-time planning cost stays below the 0.3 s the page reports
+    assert dt < 0.3
+    rs.rs_plan_free(h)
+    h, L = _compare_plan(w.specs, w.m, w.g_coll)
+    if name in ("tiny", "llama_layer", "moe"):
+        exp = _oracle_rank_blocks(L, 0)
+        for r in range(w.m):
+            a, c = rs.rs_plan_rank_blocks(h, 0, r)
+            assert (c == 0) if r not in exp else ((a, c) == exp[r])
+    rs.rs_plan_free(h)
+
+
+def test_padding_reported_for_fused_experts():
+    # 48 ranks do not divide the 2160 row blocks of the fused experts:
+    # S rounds up to 46 blocks of 128 x 2880 and the last rank stays empty.
+    w = synth.moe_bucket()
+    h = rs.rs_plan_layout(w.specs, w.m, w.g_coll)
+    S, base, pad, nblk = rs.rs_plan_bucket(h, 0)
+    assert S == 46 * 128 * 2880 and pad == 17602560 and nblk == 2161
+    assert rs.rs_plan_rank_blocks(h, 0, 47)[1] == 0
+    assert rs.rs_plan_rank_blocks(h, 0, 0) == (0, 46)
+    rs.rs_plan_free(h)
+
+
+def _expect(status, fn, *a, **k):
+    with pytest.raises(rs.RaggedShardError) as e:
+        fn(*a, **k)
+    assert e.value.status == status, str(e.value)
+
+
+def test_invalid_specs_and_arguments():
+    good = [TensorSpec("w", (8, 16), ROWS, 2)]
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout, good, 0, 16)
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout, good, 2, 0)
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout, [TensorSpec("w", (8, 16), TILE, 1, 4)], 2, 16)
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout, [TensorSpec("w", (8, 16), ROWS, 0)], 2, 16)
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout, [TensorSpec("w", (8, 0), ROWS, 2)], 2, 16)
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout, [TensorSpec("w", (8, 16), 7)], 2, 16)
+    # bucket 1 empty while bucket 2 is used
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout,
+            [TensorSpec("a", (4,), ELEMENT, bucket=0), TensorSpec("b", (4,), ELEMENT, bucket=2)],
+            2, 1)
+    _expect(rs.RS_EOVERFLOW, rs.rs_plan_layout, [TensorSpec("w", (1 << 26, 1 << 26), ROWS, 2)],
+            2, 16)
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout, good, 2, 16, order=1)
+    h = rs.rs_plan_layout(good, 2, 16)
+    _expect(rs.RS_EINVAL, rs.rs_plan_set_chunk, h, 100)
+    _expect(rs.RS_EINVAL, rs.rs_plan_set_chunk, h, 1 << 20)
+    _expect(rs.RS_EINVAL, rs.rs_plan_set_split_mode, h, 5)
+    _expect(rs.RS_EINVAL, rs.rs_plan_bucket, h, 1)
+    _expect(rs.RS_EINVAL, rs.rs_plan_rank_blocks, h, 0, 2)
+    # device calls before upload fail on the host, before any launch
+    fake = 1 << 20
+    _expect(rs.RS_ESTATE, rs.rs_pack_shard, h, 0, 0, fake, stream=0)
+    _expect(rs.RS_ESTATE, rs.rs_unpack_full, h, 0, fake, stream=0)
+    _expect(rs.RS_ESTATE, rs.rs_group_l2norm, h, 0, 0, fake, rs.RS_BF16, fake, stream=0)
+    _expect(rs.RS_ESTATE, rs.rs_adam8_step, h, 0, 0, fake, fake, fake, fake, fake, fake, stream=0)
+    _expect(rs.RS_ESTATE, rs.rs_bind_views, h, rs.RS_VIEW_F32_SRC, [fake], stream=0)
+    _expect(rs.RS_ESTATE, rs.rs_plan_check_device, h, stream=0)
+    # selection and pointer checks
+    _expect(rs.RS_EINVAL, rs.rs_pack_shard, h, 3, 0, fake, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_pack_shard, h, 0, 5, fake, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_pack_shard, h, 0, 0, fake + 2, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_group_zero, h, 0, 0, fake, 9, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_adam8_step, h, 0, 0, fake, fake + 8, fake, fake, fake, fake,
+            stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_clip_coef, fake, -1.0, fake, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_plan_upload, h, fake + 16, 1 << 30, stream=0)
+    _expect(rs.RS_ENOMEM, rs.rs_plan_upload, h, fake, 16, stream=0)
+    assert "workspace" in rs.rs_last_error()
+    rs.rs_plan_free(h)
+
+
+def test_replanning_is_deterministic():
+    # a restarted process recovers the same layout from the same inputs
+    w = synth.llama8b_tiles(layers=3)
+    a = rs.rs_plan_layout(w.specs, w.m, w.g_coll)
+    b = rs.rs_plan_layout(w.specs, w.m, w.g_coll)
+    assert rs.rs_plan_offsets(a) == rs.rs_plan_offsets(b)
+    assert rs.rs_plan_chunk_count(a) == rs.rs_plan_chunk_count(b)
+    rs.rs_plan_free(a)
+    rs.rs_plan_free(b)
