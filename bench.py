@@ -98,6 +98,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama_layer")
     ap.add_argument("--split-mode", default="cooperative", choices=["cooperative", "two_pass"])
+    ap.add_argument("--chunk", type=int, default=None, help="elements per workgroup in the step")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -120,7 +121,7 @@ def main():
     torch.cuda.set_device(dev)
     mode = rs.RS_SPLIT_COOPERATIVE if args.split_mode == "cooperative" else rs.RS_SPLIT_TWO_PASS
     t0 = time.perf_counter()
-    plan = rs.Plan(w.specs, w.m, w.g_coll, split_mode=mode)
+    plan = rs.Plan(w.specs, w.m, w.g_coll, chunk=args.chunk, split_mode=mode)
     plan_s = time.perf_counter() - t0
     plan.upload()
     total, nblk = plan.total, plan.n_blocks
@@ -241,6 +242,7 @@ def main():
             "padding": plan.padding[0],
             "quant_blocks": nblk,
             "split_mode": args.split_mode,
+            "chunk_elems": args.chunk or 8192,
             "planner_s": round(plan_s, 4),
         },
         "step_params_per_s": round(real / (per_op["adam8_step"] * 1e-3), 1),

@@ -138,12 +138,14 @@ rs_status rs_plan_rank_blocks(const rs_plan* plan, int32_t bucket, int32_t rank,
                               int64_t* count);
 
 /* Maximum elements one workgroup handles in the step (a multiple of 16 in
- * 64..16384, default 16384).  Larger blocks are split into chunks.  Must be
+ * 64..16384, default 8192).  Larger blocks are split into chunks.  Must be
  * called before rs_plan_upload.  Errors: RS_EINVAL, RS_ESTATE (uploaded). */
 rs_status rs_plan_set_chunk(rs_plan* plan, int64_t chunk_elems);
 
-/* RS_SPLIT_TWO_PASS (default) or RS_SPLIT_COOPERATIVE; may change at any
- * time between calls. */
+/* RS_SPLIT_COOPERATIVE (default) or RS_SPLIT_TWO_PASS; may change at any
+ * time between calls.  The cooperative mode falls back to two launches when
+ * the device cannot hold every chunk of the largest split block twice over
+ * (occupancy of the step kernel times the compute units). */
 rs_status rs_plan_set_split_mode(rs_plan* plan, int32_t mode);
 
 /* Number of chunks of the step's work table (valid after the chunk size is

@@ -267,7 +267,7 @@ class Plan:
     """Owns one rs_plan handle and (after upload) its device workspace."""
 
     def __init__(self, specs, m: int, g_coll: int, chunk: Optional[int] = None,
-                 split_mode: int = RS_SPLIT_TWO_PASS):
+                 split_mode: int = RS_SPLIT_COOPERATIVE):
         self.h = rs_plan_layout(specs, m, g_coll)
         self.specs = list(specs)
         if chunk is not None:

@@ -7,16 +7,37 @@
 // int8 over 127 levels, v as uint8 over 255 levels) and the AdamW constants
 // are this library's definition; the pages do not fix them.
 //
-// One workgroup of 1024 threads handles one chunk of <= 16384 elements;
-// each lane owns 16 consecutive elements (four 16-byte fp32 loads, two for
-// the bf16 gradient, one each for the int8/uint8 codes).  The new block
-// absmax is a wave butterfly (DPP/permute) plus an LDS pass over the 16
-// waves; the lane keeps its 16 m and v values in registers until the absmax
-// is known, so every byte is read once and written once.  Blocks larger than
-// one chunk are split over several workgroups and their absmax is combined
-// either by a first launch that writes per-chunk partials (two-pass) or by
-// device-scope counters inside one launch (cooperative).
+// One workgroup handles one chunk (<= 16 elements per thread).  Wave w of the
+// workgroup covers chunk elements [1024 w, 1024 w + 1024) as four 256-element
+// slices; lane l owns elements 256 k + 4 l .. +3 (k = 0..3), so each load and
+// store instruction of a wave touches one contiguous span (1 KiB of fp32,
+// 512 B of bf16, 256 B of codes).  The lane keeps its 16 new m and v values
+// in registers until the block absmax is known (wave butterfly, then LDS
+// across waves), so every byte is read once and written once.
+//
+// Arithmetic: the update follows the fixed binary32 order of the
+// definition with correctly rounded '/' and sqrt and no FMA contraction, so
+// m, v and the parameters match a correctly rounded evaluation bit for bit.
+// The quantisation ratio m / absmax is the correctly rounded quotient too,
+// formed from the block's correctly rounded reciprocal y and one residual
+// step q = q0 + (m - q0*a)*y with q0 = m*y (Markstein's correction): exact
+// for every quotient that can reach a nonzero code once absmax >= 2^-60;
+// smaller absmax values take the plain division.
+//
+// Blocks larger than one chunk are split over several workgroups; their
+// absmax is combined either by a first launch that writes per-chunk partials
+// (two-pass) or inside one launch through device-scope counters
+// (cooperative).  In the cooperative launch the chunks of a block are
+// consecutive workgroups.  Workgroups are dispatched in index order on each
+// XCD, so a block's missing chunk can only be undispatched while its XCD is
+// full of workgroups whose indices lie inside that block's span; with P
+// chunks per block that needs more than P / 8 resident workgroups per XCD,
+// and the launch uses this mode only when the device holds twice the chunks
+// of the largest block.  Each wait is bounded and reports a timeout through
+// the device status word if it ever gives up.
 #include <hip/hip_runtime.h>
+
+#include <mutex>
 
 #include "launch.hpp"
 #include "raggedshard.h"
@@ -27,7 +48,10 @@ namespace {
 
 enum { MODE_PARTIAL = 0, MODE_MAIN = 1, MODE_COOP = 2 };
 
-// Bounded wait for the other chunks of a block (about 50 ms of sleeps; a
+// 4-element groups per lane: a lane owns 4 * kGroups elements of its chunk.
+constexpr int kGroups = kElemsPerLane / 4;
+
+// Bounded wait for the other chunks of a block (tens of ms of sleeps; a
 // normal wait is microseconds).  After any timeout every later wait of the
 // launch gives up at once, so a failed launch still ends quickly.
 constexpr uint32_t kSpinLimit = 1u << 20;
@@ -39,44 +63,73 @@ struct StepArgs {
     int64_t nwg;
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
     uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-__device__ __forceinline__ uint32_t quant_m(float m, float a) {
-    if (a == 0.0f) return 0u;
-    float r = rintf((m / a) * 127.0f);
-    r = fminf(fmaxf(r, -127.0f), 127.0f);
-    return (uint32_t)(int32_t)r & 0xffu;
+// Reciprocal used by the quantiser: correctly rounded 1/a, 0 for a == 0.
+__device__ __forceinline__ float quant_recip(float a) { return a == 0.0f ? 0.0f : 1.0f / a; }
+
+// Blocks whose absmax is below 2^-60 (but not 0) take the plain division.
+__device__ __forceinline__ bool quant_slow(float a) { return a < 0x1p-60f && a > 0.0f; }
+
+// m / a by Markstein's correction from y = RN(1/a); correctly rounded for
+// every quotient that can give a nonzero code when !quant_slow(a), and 0
+// for a == 0 (y = 0, m = 0).
+__device__ __forceinline__ float ratio_fast(float m, float a, float y) {
+    const float q0 = m * y;
+    const float r = __builtin_fmaf(-q0, a, m);
+    return __builtin_fmaf(r, y, q0);
 }
 
-__device__ __forceinline__ uint32_t quant_v(float v, float a) {
-    if (a == 0.0f) return 0u;
-    float r = rintf((v / a) * 255.0f);
-    r = fminf(fmaxf(r, 0.0f), 255.0f);
-    return (uint32_t)r;
+// Correctly rounded m / a (see the file comment); a >= 0, y = quant_recip(a).
+__device__ __forceinline__ float ratio(float m, float a, float y) {
+    if (quant_slow(a)) return m / a;
+    return ratio_fast(m, a, y);
 }
 
-// The AdamW update of one element (binary32, fixed operation order; the
-// build disables FMA contraction so products and sums round separately).
+__device__ __forceinline__ uint32_t code_m(float m, float a, float y) {
+    float c = rintf(ratio(m, a, y) * 127.0f);
+    c = fminf(fmaxf(c, -127.0f), 127.0f);
+    return (uint32_t)(int32_t)c & 0xffu;
+}
+
+__device__ __forceinline__ uint32_t code_v(float v, float a, float y) {
+    float c = rintf(ratio(v, a, y) * 255.0f);
+    c = fminf(fmaxf(c, 0.0f), 255.0f);
+    return (uint32_t)c;
+}
+
 struct Elem {
     float m, v, th;
 };
 
+// One element of AdamW in the fixed binary32 order of the definition.
 __device__ __forceinline__ Elem update(const StepScalars& sc, float theta, float g, float mh,
                                        float vh) {
     Elem e;
     e.m = (sc.beta1 * mh) + (sc.omega1 * g);
     e.v = (sc.beta2 * vh) + (sc.omega2 * (g * g));
-    float t = theta * sc.c_decay;
-    float den = (sqrtf(e.v) * sc.kappa) + sc.eps;
-    e.th = t - (sc.step_size * (e.m / den));
+    const float den = (sqrtf(e.v) * sc.kappa) + sc.eps;
+    e.th = (theta * sc.c_decay) - (sc.step_size * (e.m / den));
     return e;
+}
+
+// Moments of one element (definition order, binary32).
+__device__ __forceinline__ void moments(const StepScalars& sc, float g, float mh, float vh,
+                                        float& m, float& v) {
+    m = (sc.beta1 * mh) + (sc.omega1 * g);
+    v = (sc.beta2 * vh) + (sc.omega2 * (g * g));
+}
+
+__device__ __forceinline__ float param(const StepScalars& sc, float theta, float m, float sq) {
+    const float den = (sq * sc.kappa) + sc.eps;
+    return (theta * sc.c_decay) - (sc.step_size * (m / den));
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -86,9 +139,11 @@ __device__ __forceinline__ float wave_max(float x) {
 }
 
 // Max over the workgroup of (a, b); every thread gets the result.
+template <int NT>
 __device__ __forceinline__ void wg_max2(float& a, float& b, float* red) {
     a = wave_max(a);
     b = wave_max(b);
+    if (NT == 64) return;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) {
         red[2 * wave] = a;
@@ -96,8 +151,8 @@ __device__ __forceinline__ void wg_max2(float& a, float& b, float* red) {
     }
     __syncthreads();
     float x = 0.0f, y = 0.0f;
-    const int nw = blockDim.x >> 6;
-    for (int i = 0; i < nw; ++i) {
+#pragma unroll
+    for (int i = 0; i < NT / 64; ++i) {
         x = fmaxf(x, red[2 * i]);
         y = fmaxf(y, red[2 * i + 1]);
     }
@@ -112,223 +167,323 @@ __device__ __forceinline__ int64_t chunk_of(const Ranges& r, int64_t wg) {
     return r.lo[i] + (wg - r.wg0[i]);
 }
 
+// The chunks of a split block meet through a slot of device-scope atomics
+// (the running maxima, the arrival count; a status word reports timeouts).
+// Agent-scope atomic loads read the coherent value, so no cache-wide
+// release / acquire is needed: the maxima are made complete before the
+// arrival is counted by waiting for the issuing wave's outstanding memory
+// operations, and the wait polls with relaxed loads (a release / acquire
+// pair would write back and invalidate the XCD's L2 on every arrival and
+// every poll).  coop_publish runs on thread 0 right after the chunk's
+// maxima are known; the parameter update runs before coop_wait, so the
+// other chunks' arrivals overlap with it.
+
+struct CoopTicket {
+    uint64_t target;
+    int slot;
+};
+
+__device__ __forceinline__ CoopTicket coop_publish(const StepBuffers& B, const ChunkDesc& d,
+                                                   int64_t c, float am, float av) {
+    CoopSlot* cs = &B.coop[c - d.part];
+    const uint64_t np = (uint64_t)d.nparts;
+    const uint64_t a0 = __hip_atomic_load(&cs->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t gen = a0 / np;
+    const int slot = (int)(gen & 1u);
+    __hip_atomic_fetch_max(&cs->amax_m[slot], __float_as_uint(am), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_fetch_max(&cs->amax_v[slot], __float_as_uint(av), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&cs->amax_m[slot ^ 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&cs->amax_v[slot ^ 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_s_waitcnt(0);  // the maxima are performed before the arrival counts
+    __hip_atomic_fetch_add(&cs->arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return CoopTicket{(gen + 1) * np, slot};
+}
+
+// Thread 0 waits for every chunk of the block (bounded) and returns the
+// block maxima.
+__device__ __forceinline__ void coop_wait(const StepBuffers& B, const ChunkDesc& d, int64_t c,
+                                          CoopTicket t, float& am, float& av) {
+    CoopSlot* cs = &B.coop[c - d.part];
+    uint32_t spins = 0;
+    while (__hip_atomic_load(&cs->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < t.target) {
+        __builtin_amdgcn_s_sleep(1);
+        ++spins;
+        if ((spins & 255u) == 0 &&
+            __hip_atomic_load(&B.counters->timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
+            break;
+        if (spins > kSpinLimit) {
+            __hip_atomic_fetch_or(&B.counters->timeout, 1u, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+            break;
+        }
+    }
+    am = __uint_as_float(
+        __hip_atomic_load(&cs->amax_m[t.slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    av = __uint_as_float(
+        __hip_atomic_load(&cs->amax_v[t.slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+
 // ------------------------------------------------------------ vector path
 
-template <int MODE>
+template <int MODE, int NT, int KG>
 __device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, float s,
                           const float* dqm, const float* dqv, float* red) {
+    constexpr int WSPAN = 256 * KG;  // chunk elements covered by one wave
     const StepBuffers& B = a.b;
     const StepScalars& sc = a.sc;
     const bool split = d.nparts > 1;
     if (MODE == MODE_PARTIAL && !split) return;
-    const int v = threadIdx.x;
-    const int vpr = d.cols >> 4;
-    const int nvec = d.rows * vpr;
-    const bool act = v < nvec;
-    int64_t p;
-    if (d.rows == 1) {
-        p = d.pos + int64_t(v) * kVec;
-    } else {
-        int row = v / vpr;
-        p = d.pos + int64_t(row) * d.ld + int64_t(v - row * vpr) * kVec;
-    }
-    const bool multi = d.vpb_log2 >= 0;
-    const int64_t blk = multi ? d.blk + (v >> d.vpb_log2) : d.blk;
+    const bool run = d.run_log2 >= 0;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int n = d.rows * d.cols;
+    // row = e / cols via a multiply-high (exact for e, cols < 2^16)
+    const uint32_t magic = d.rows > 1 ? (0xffffffffu / (uint32_t)d.cols) + 1u : 0u;
 
-    // old absmax of the block(s)
-    float am_old = 0.0f, av_old = 0.0f;
+    // Uniform chunk bases plus 32-bit lane offsets (tile chunks keep
+    // rows * ld < 2^30), so loads and stores use the scalar-base address mode.
+    float* __restrict__ th_b = B.theta + d.pos;
+    const uint16_t* __restrict__ g_b = B.grad + d.pos;
+    int8_t* __restrict__ qm_b = B.qm + d.pos;
+    uint8_t* __restrict__ qv_b = B.qv + d.pos;
+    uint16_t* __restrict__ out_b = B.out ? B.out + d.pos : nullptr;
+    uint32_t p[KG];
+    bool act[KG];
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        const int e = wave * WSPAN + 256 * k + 4 * lane;
+        act[k] = e < n;
+        if (d.rows == 1) {
+            p[k] = (uint32_t)e;
+        } else {
+            const uint32_t row = __umulhi((uint32_t)e, magic);
+            p[k] = row * (uint32_t)d.ld + ((uint32_t)e - row * (uint32_t)d.cols);
+        }
+    }
+
+    // old absmax of the block(s) this lane touches
+    float amo[KG], avo[KG];
     if (MODE == MODE_MAIN && split) {
         const ChunkPartial cp = B.cpart[c];
-        am_old = cp.old_m;
-        av_old = cp.old_v;
-    } else if (act) {
-        am_old = B.amax_m[blk];
-        av_old = B.amax_v[blk];
-    }
-
-    // final absmax known up front in the second launch of the two-pass mode
-    float fin_m = 0.0f, fin_v = 0.0f;
-    if (MODE == MODE_MAIN && split) {
-        const int64_t c0 = c - d.part;
-        for (int q = 0; q < d.nparts; ++q) {
-            const ChunkPartial cp = B.cpart[c0 + q];
-            fin_m = fmaxf(fin_m, cp.pm);
-            fin_v = fmaxf(fin_v, cp.pv);
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            amo[k] = cp.old_m;
+            avo[k] = cp.old_v;
+        }
+    } else if (run) {
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            const int64_t blk = d.blk + ((wave * WSPAN + 256 * k + 4 * lane) >> d.run_log2);
+            amo[k] = act[k] ? B.amax_m[blk] : 0.0f;
+            avo[k] = act[k] ? B.amax_v[blk] : 0.0f;
+        }
+    } else {
+        const float x = B.amax_m[d.blk], y = B.amax_v[d.blk];
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            amo[k] = x;
+            avo[k] = y;
         }
     }
 
-    float M[kVec], V[kVec];
-    float lam = 0.0f, lav = 0.0f;
-    if (act) {
-        const uint4 g0 = *reinterpret_cast<const uint4*>(B.grad + p);
-        const uint4 g1 = *reinterpret_cast<const uint4*>(B.grad + p + 8);
-        const uint4 qm = *reinterpret_cast<const uint4*>(B.qm + p);
-        const uint4 qv = *reinterpret_cast<const uint4*>(B.qv + p);
-        const uint32_t gw[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-        const uint32_t mw[4] = {qm.x, qm.y, qm.z, qm.w};
-        const uint32_t vw[4] = {qv.x, qv.y, qv.z, qv.w};
-        float th[kVec];
-        if (MODE != MODE_PARTIAL) {
-            const float4* tp = reinterpret_cast<const float4*>(B.theta + p);
+    // All loads first: the buffers may alias as far as the compiler knows, so
+    // without this each 4-element slice would wait for the previous slice's
+    // stores and a wave would pay four memory round trips instead of one.
+    float4 TH[KG];
+    uint2 GW[KG];
+    uint32_t CM[KG], CV[KG];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float4 t = tp[i];
-                th[4 * i] = t.x;
-                th[4 * i + 1] = t.y;
-                th[4 * i + 2] = t.z;
-                th[4 * i + 3] = t.w;
+    for (int k = 0; k < KG; ++k) {
+        if (act[k]) {
+            GW[k] = *reinterpret_cast<const uint2*>(g_b + p[k]);
+            CM[k] = *reinterpret_cast<const uint32_t*>(qm_b + p[k]);
+            CV[k] = *reinterpret_cast<const uint32_t*>(qv_b + p[k]);
+            TH[k] = MODE != MODE_PARTIAL ? *reinterpret_cast<const float4*>(th_b + p[k])
+                                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        } else {
+            GW[k] = make_uint2(0u, 0u);
+            CM[k] = CV[k] = 0u;
+            TH[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        }
+    }
+
+    float M[4 * KG], V[4 * KG];
+    float lm[KG], lv[KG];
+#pragma unroll
+    for (int k = 0; k < KG; ++k) lm[k] = lv[k] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        const float g[4] = {bf16_lo(GW[k].x) * s, bf16_hi(GW[k].x) * s, bf16_lo(GW[k].y) * s,
+                            bf16_hi(GW[k].y) * s};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const float mh = dqm[(CM[k] >> (8 * j)) & 0xffu] * amo[k];
+            const float vh = dqv[(CV[k] >> (8 * j)) & 0xffu] * avo[k];
+            moments(sc, g[j], mh, vh, M[4 * k + j], V[4 * k + j]);
+            lm[k] = fmaxf(lm[k], fabsf(M[4 * k + j]));
+            lv[k] = fmaxf(lv[k], V[4 * k + j]);
+        }
+    }
+    // new absmax per block
+    float am[KG], av[KG];
+    CoopTicket ticket{0, 0};
+    bool wait = false;
+    if (run) {
+        // blocks of (1 << run_log2) elements = (1 << run_log2) / 4 lanes of one slice
+        const int lanes = (1 << d.run_log2) >> 2;
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            am[k] = lm[k];
+            av[k] = lv[k];
+            for (int off = 1; off < lanes; off <<= 1) {
+                am[k] = fmaxf(am[k], __shfl_xor(am[k], off, 64));
+                av[k] = fmaxf(av[k], __shfl_xor(av[k], off, 64));
+            }
+        }
+    } else {
+        float x, y;
+        if (MODE == MODE_MAIN && split) {
+            x = 0.0f;
+            y = 0.0f;
+            const int64_t c0 = c - d.part;
+            for (int q = 0; q < d.nparts; ++q) {
+                const ChunkPartial cp = B.cpart[c0 + q];
+                x = fmaxf(x, cp.pm);
+                y = fmaxf(y, cp.pv);
             }
         } else {
+            x = lm[0];
+            y = lv[0];
 #pragma unroll
-            for (int j = 0; j < kVec; ++j) th[j] = 0.0f;
-        }
-#pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            const uint32_t w = gw[j >> 1];
-            const float g = ((j & 1) ? bf16_hi(w) : bf16_lo(w)) * s;
-            const uint32_t cm = (mw[j >> 2] >> (8 * (j & 3))) & 0xffu;
-            const uint32_t cv = (vw[j >> 2] >> (8 * (j & 3))) & 0xffu;
-            const float mh = dqm[cm] * am_old;
-            const float vh = dqv[cv] * av_old;
-            Elem e = update(sc, th[j], g, mh, vh);
-            M[j] = e.m;
-            V[j] = e.v;
-            th[j] = e.th;
-            lam = fmaxf(lam, fabsf(e.m));
-            lav = fmaxf(lav, e.v);
-        }
-        if (MODE != MODE_PARTIAL) {
-            float4* tp = reinterpret_cast<float4*>(B.theta + p);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                tp[i] = make_float4(th[4 * i], th[4 * i + 1], th[4 * i + 2], th[4 * i + 3]);
-            if (B.out) {
-                uint32_t o[8];
-#pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    o[i] = (uint32_t)f32_to_bf16(th[2 * i]) | ((uint32_t)f32_to_bf16(th[2 * i + 1]) << 16);
-                uint4* op = reinterpret_cast<uint4*>(B.out + p);
-                op[0] = make_uint4(o[0], o[1], o[2], o[3]);
-                op[1] = make_uint4(o[4], o[5], o[6], o[7]);
+            for (int k = 1; k < KG; ++k) {
+                x = fmaxf(x, lm[k]);
+                y = fmaxf(y, lv[k]);
             }
-        }
-    }
-
-    // new absmax
-    float am, av;
-    if (multi) {
-        // blocks of (1 << vpb_log2) lanes inside one wave
-        am = lam;
-        av = lav;
-        for (int off = 1; off < (1 << d.vpb_log2); off <<= 1) {
-            am = fmaxf(am, __shfl_xor(am, off, 64));
-            av = fmaxf(av, __shfl_xor(av, off, 64));
-        }
-    } else if (MODE == MODE_MAIN && split) {
-        am = fin_m;
-        av = fin_v;
-    } else {
-        am = lam;
-        av = lav;
-        wg_max2(am, av, red);
-        if (split) {
-            if (MODE == MODE_PARTIAL) {
-                if (threadIdx.x == 0) B.cpart[c] = ChunkPartial{am, av, am_old, av_old};
-                return;
-            }
-            // MODE_COOP: meet the other chunks of this block
-            if (threadIdx.x == 0) {
-                CoopSlot* cs = &B.coop[c - d.part];
-                const uint64_t np = (uint64_t)d.nparts;
-                const uint64_t a0 = __hip_atomic_load(&cs->arrive, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t gen = a0 / np;
-                const int slot = (int)(gen & 1u);
-                __hip_atomic_fetch_max(&cs->amax_m[slot], __float_as_uint(am), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_fetch_max(&cs->amax_v[slot], __float_as_uint(av), __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&cs->amax_m[slot ^ 1], 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&cs->amax_v[slot ^ 1], 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_fetch_add(&cs->arrive, (uint64_t)1, __ATOMIC_RELEASE,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t target = (gen + 1) * np;
-                uint32_t spins = 0;
-                while (__hip_atomic_load(&cs->arrive, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT) <
-                       target) {
-                    __builtin_amdgcn_s_sleep(2);
-                    ++spins;
-                    if ((spins & 255u) == 0 &&
-                        __hip_atomic_load(&B.counters->timeout, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT) != 0)
-                        break;
-                    if (spins > kSpinLimit) {
-                        __hip_atomic_fetch_or(&B.counters->timeout, 1u, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
-                        break;
-                    }
+            wg_max2<NT>(x, y, red);
+            if (split) {
+                if (MODE == MODE_PARTIAL) {
+                    if (threadIdx.x == 0) B.cpart[c] = ChunkPartial{x, y, amo[0], avo[0]};
+                    return;
                 }
-                red[0] = __uint_as_float(__hip_atomic_load(&cs->amax_m[slot], __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT));
-                red[1] = __uint_as_float(__hip_atomic_load(&cs->amax_v[slot], __ATOMIC_RELAXED,
-                                                           __HIP_MEMORY_SCOPE_AGENT));
+                if (threadIdx.x == 0) ticket = coop_publish(B, d, c, x, y);
+                wait = true;
             }
-            __syncthreads();
-            am = red[0];
-            av = red[1];
+        }
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            am[k] = x;
+            av[k] = y;
         }
     }
 
-    if (act) {
-        uint32_t qmw[4] = {0, 0, 0, 0}, qvw[4] = {0, 0, 0, 0};
+    if (MODE != MODE_PARTIAL) {
 #pragma unroll
-        for (int j = 0; j < kVec; ++j) {
-            qmw[j >> 2] |= quant_m(M[j], am) << (8 * (j & 3));
-            qvw[j >> 2] |= quant_v(V[j], av) << (8 * (j & 3));
+        for (int k = 0; k < KG; ++k) {
+            if (!act[k]) continue;
+            float t[4] = {TH[k].x, TH[k].y, TH[k].z, TH[k].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) t[j] = param(sc, t[j], M[4 * k + j], sqrtf(V[4 * k + j]));
+            *reinterpret_cast<float4*>(th_b + p[k]) = make_float4(t[0], t[1], t[2], t[3]);
+            if (out_b) {
+                const uint2 o = make_uint2(f32_to_bf16(t[0]) | (f32_to_bf16(t[1]) << 16),
+                                           f32_to_bf16(t[2]) | (f32_to_bf16(t[3]) << 16));
+                *reinterpret_cast<uint2*>(out_b + p[k]) = o;
+            }
         }
-        *reinterpret_cast<uint4*>(B.qm + p) = make_uint4(qmw[0], qmw[1], qmw[2], qmw[3]);
-        *reinterpret_cast<uint4*>(B.qv + p) = make_uint4(qvw[0], qvw[1], qvw[2], qvw[3]);
-        const bool writer = multi ? ((v & ((1 << d.vpb_log2) - 1)) == 0) : (v == 0 && d.part == 0);
-        if (writer) {
-            B.amax_m[blk] = am;
-            B.amax_v[blk] = av;
+    }
+
+    if (wait) {
+        // MODE_COOP, split block: the other chunks' maxima
+        if (threadIdx.x == 0) {
+            float x, y;
+            coop_wait(B, d, c, ticket, x, y);
+            red[0] = x;
+            red[1] = y;
         }
+        __syncthreads();
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            am[k] = red[0];
+            av[k] = red[1];
+        }
+    }
+
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        if (!act[k]) continue;
+        const float ym = quant_recip(am[k]), yv = quant_recip(av[k]);
+        uint32_t qmw = 0u, qvw = 0u;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            // |m| <= absmax bounds the codes: no clamp; int8 via a +128 offset
+            qmw = __builtin_amdgcn_cvt_pk_u8_f32(
+                rintf(ratio_fast(M[4 * k + j], am[k], ym) * 127.0f) + 128.0f, j, qmw);
+            qvw = __builtin_amdgcn_cvt_pk_u8_f32(
+                rintf(ratio_fast(V[4 * k + j], av[k], yv) * 255.0f), j, qvw);
+        }
+        qmw ^= 0x80808080u;
+        if (__builtin_expect(quant_slow(am[k]) || quant_slow(av[k]), 0)) {
+            // absmax below 2^-60: plain division
+            qmw = 0u;
+            qvw = 0u;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                qmw |= code_m(M[4 * k + j], am[k], ym) << (8 * j);
+                qvw |= code_v(V[4 * k + j], av[k], yv) << (8 * j);
+            }
+        }
+        *reinterpret_cast<uint32_t*>(qm_b + p[k]) = qmw;
+        *reinterpret_cast<uint32_t*>(qv_b + p[k]) = qvw;
+        if (run) {
+            const int lanes = (1 << d.run_log2) >> 2;
+            if ((lane & (lanes - 1)) == 0) {
+                const int64_t blk = d.blk + ((wave * WSPAN + 256 * k + 4 * lane) >> d.run_log2);
+                B.amax_m[blk] = am[k];
+                B.amax_v[blk] = av[k];
+            }
+        }
+    }
+    if (!run && threadIdx.x == 0 && d.part == 0) {
+        B.amax_m[d.blk] = am[0];
+        B.amax_v[d.blk] = av[0];
     }
 }
 
 // --------------------------------------------------- generic block paths
 
 // One whole block of any shape or alignment, two sweeps.
+template <int NT>
 __device__ void scalar_chunk(const ChunkDesc& d, const StepArgs& a, float s, const float* dqm,
                              const float* dqv, float* red) {
     const StepBuffers& B = a.b;
     const int64_t n = int64_t(d.rows) * d.cols;
     const float am_old = B.amax_m[d.blk], av_old = B.amax_v[d.blk];
     float lam = 0.0f, lav = 0.0f;
-    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+    for (int64_t e = threadIdx.x; e < n; e += NT) {
         const int64_t r = e / d.cols;
         const int64_t p = d.pos + r * d.ld + (e - r * d.cols);
         const float g = __uint_as_float(uint32_t(B.grad[p]) << 16) * s;
         const float mh = dqm[uint8_t(B.qm[p])] * am_old;
         const float vh = dqv[B.qv[p]] * av_old;
-        Elem el = update(a.sc, 0.0f, g, mh, vh);
+        const Elem el = update(a.sc, 0.0f, g, mh, vh);
         lam = fmaxf(lam, fabsf(el.m));
         lav = fmaxf(lav, el.v);
     }
-    wg_max2(lam, lav, red);
-    for (int64_t e = threadIdx.x; e < n; e += blockDim.x) {
+    wg_max2<NT>(lam, lav, red);
+    const float ym = quant_recip(lam), yv = quant_recip(lav);
+    for (int64_t e = threadIdx.x; e < n; e += NT) {
         const int64_t r = e / d.cols;
         const int64_t p = d.pos + r * d.ld + (e - r * d.cols);
         const float g = __uint_as_float(uint32_t(B.grad[p]) << 16) * s;
         const float mh = dqm[uint8_t(B.qm[p])] * am_old;
         const float vh = dqv[B.qv[p]] * av_old;
-        Elem el = update(a.sc, B.theta[p], g, mh, vh);
+        const Elem el = update(a.sc, B.theta[p], g, mh, vh);
         B.theta[p] = el.th;
-        if (B.out) B.out[p] = f32_to_bf16(el.th);
-        B.qm[p] = (int8_t)quant_m(el.m, lam);
-        B.qv[p] = (uint8_t)quant_v(el.v, lav);
+        if (B.out) B.out[p] = (uint16_t)f32_to_bf16(el.th);
+        B.qm[p] = (int8_t)code_m(el.m, lam, ym);
+        B.qv[p] = (uint8_t)code_v(el.v, lav, yv);
     }
     if (threadIdx.x == 0) {
         B.amax_m[d.blk] = lam;
@@ -336,82 +491,101 @@ __device__ void scalar_chunk(const ChunkDesc& d, const StepArgs& a, float s, con
     }
 }
 
-// A run of single-element blocks.
+// A run of single-element blocks: the absmax is the element itself, so the
+// codes are +-127 / 255 (or 0) and the state is lossless.
+template <int NT>
 __device__ void elem_chunk(const ChunkDesc& d, const StepArgs& a, float s, const float* dqm,
                            const float* dqv) {
     const StepBuffers& B = a.b;
-    for (int e = threadIdx.x; e < d.cols; e += blockDim.x) {
+    for (int e = threadIdx.x; e < d.cols; e += NT) {
         const int64_t p = d.pos + e;
         const int64_t blk = d.blk + e;
         const float g = __uint_as_float(uint32_t(B.grad[p]) << 16) * s;
         const float mh = dqm[uint8_t(B.qm[p])] * B.amax_m[blk];
         const float vh = dqv[B.qv[p]] * B.amax_v[blk];
-        Elem el = update(a.sc, B.theta[p], g, mh, vh);
+        const Elem el = update(a.sc, B.theta[p], g, mh, vh);
         B.theta[p] = el.th;
-        if (B.out) B.out[p] = f32_to_bf16(el.th);
+        if (B.out) B.out[p] = (uint16_t)f32_to_bf16(el.th);
         const float am = fabsf(el.m), av = el.v;
-        B.qm[p] = (int8_t)quant_m(el.m, am);
-        B.qv[p] = (uint8_t)quant_v(el.v, av);
+        B.qm[p] = (int8_t)code_m(el.m, am, quant_recip(am));
+        B.qv[p] = (uint8_t)code_v(el.v, av, quant_recip(av));
         B.amax_m[blk] = am;
         B.amax_v[blk] = av;
     }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(kStepThreads) void adam8_kernel(StepArgs a) {
+template <int MODE, int NT>
+__global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
     __shared__ float dqm[256], dqv[256];
-    __shared__ float red[2 * (kStepThreads / 64)];
-    __shared__ int64_t ticket_sh;
+    __shared__ float red[2 * (NT / 64) + 2];
     // dequantisation tables: code -> code / 127 (int8), code / 255 (uint8)
-    if (threadIdx.x < 256) {
-        dqm[threadIdx.x] = (float)(int8_t)(uint8_t)threadIdx.x / 127.0f;
-        dqv[threadIdx.x] = (float)threadIdx.x / 255.0f;
+    for (int i = threadIdx.x; i < 256; i += NT) {
+        dqm[i] = (float)(int8_t)(uint8_t)i / 127.0f;
+        dqv[i] = (float)i / 255.0f;
     }
-    int64_t wg = blockIdx.x;
-    if (MODE == MODE_COOP) {
-        // chunks are claimed in table order by running workgroups, so a
-        // block's missing chunks are always claimable (no wait cycle)
-        if (threadIdx.x == 0)
-            ticket_sh = (int64_t)__hip_atomic_fetch_add(&a.b.counters->ticket, 1u,
-                                                        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
-        wg = ticket_sh;
-    } else {
-        __syncthreads();
+    __syncthreads();
+    const int64_t wg = blockIdx.x;
+    const int64_t c = chunk_of(a.r, wg);
+    const ChunkDesc d = a.b.chunks[c];
+    const float s = a.b.gscale ? *a.b.gscale : 1.0f;
+    if (d.kind == KIND_VEC) {
+        vec_chunk<MODE, NT, kGroups>(d, c, a, s, dqm, dqv, red);
+    } else if (MODE != MODE_PARTIAL) {
+        if (d.kind == KIND_SCALAR)
+            scalar_chunk<NT>(d, a, s, dqm, dqv, red);
+        else
+            elem_chunk<NT>(d, a, s, dqm, dqv);
     }
-    if (wg < a.nwg) {
-        const int64_t c = chunk_of(a.r, wg);
-        const ChunkDesc d = a.b.chunks[c];
-        const float s = a.b.gscale ? *a.b.gscale : 1.0f;
-        if (d.kind == KIND_VEC) {
-            vec_chunk<MODE>(d, c, a, s, dqm, dqv, red);
-        } else if (MODE != MODE_PARTIAL) {
-            if (d.kind == KIND_SCALAR)
-                scalar_chunk(d, a, s, dqm, dqv, red);
-            else
-                elem_chunk(d, a, s, dqm, dqv);
-        }
+}
+
+// Workgroups of one cooperative launch that are sure to be resident together.
+template <int NT>
+int coop_capacity() {
+    static std::mutex mu;
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int per_cu = 0, ncu = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+                &per_cu, reinterpret_cast<const void*>(adam8_kernel<MODE_COOP, NT>), NT, 0) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cached[dev] = per_cu * ncu;
     }
-    if (MODE == MODE_COOP) {
-        __syncthreads();
-        if (threadIdx.x == 0) {
-            uint32_t prev = __hip_atomic_fetch_add(&a.b.counters->done, 1u, __ATOMIC_ACQ_REL,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-            if (prev + 1 == (uint32_t)a.nwg) {
-                // last workgroup of the launch: reset for the next one
-                __hip_atomic_store(&a.b.counters->ticket, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&a.b.counters->done, 0u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-            }
-        }
+    return cached[dev];
+}
+
+template <int NT>
+hipError_t launch_nt(const StepArgs& a, int32_t mode, int32_t max_nparts, hipStream_t s) {
+    const dim3 grid((unsigned)a.nwg), block(NT);
+    // cooperative only with a 2x margin on residency (other work may share the device)
+    if (mode == RS_SPLIT_COOPERATIVE && max_nparts > 1 && 2 * max_nparts <= coop_capacity<NT>()) {
+        hipLaunchKernelGGL((adam8_kernel<MODE_COOP, NT>), grid, block, 0, s, a);
+        return hipGetLastError();
     }
+    hipLaunchKernelGGL((adam8_kernel<MODE_PARTIAL, NT>), grid, block, 0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((adam8_kernel<MODE_MAIN, NT>), grid, block, 0, s, a);
+    return hipGetLastError();
 }
 
 }  // namespace
 
+int step_threads(int64_t chunk_elems) {
+    const int64_t lanes = (chunk_elems + kElemsPerLane - 1) / kElemsPerLane;
+    if (lanes <= 64) return 64;
+    if (lanes <= 128) return 128;
+    if (lanes <= 256) return 256;
+    if (lanes <= 512) return 512;
+    return 1024;
+}
+
 hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const StepScalars& sc,
-                        int32_t mode, hipStream_t s) {
+                        int32_t mode, int64_t chunk_elems, int32_t max_nparts, hipStream_t s) {
     StepArgs a;
     a.r = chunk_ranges;
     int64_t total = 0;
@@ -425,16 +599,18 @@ hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const 
     a.nwg = total;
     if (total == 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)total), block(kStepThreads);
-    if (mode == RS_SPLIT_COOPERATIVE) {
-        hipLaunchKernelGGL(adam8_kernel<MODE_COOP>, grid, block, 0, s, a);
-        return hipGetLastError();
+    switch (step_threads(chunk_elems)) {
+    case 64:
+        return launch_nt<64>(a, mode, max_nparts, s);
+    case 128:
+        return launch_nt<128>(a, mode, max_nparts, s);
+    case 256:
+        return launch_nt<256>(a, mode, max_nparts, s);
+    case 512:
+        return launch_nt<512>(a, mode, max_nparts, s);
+    default:
+        return launch_nt<1024>(a, mode, max_nparts, s);
     }
-    hipLaunchKernelGGL(adam8_kernel<MODE_PARTIAL>, grid, block, 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(adam8_kernel<MODE_MAIN>, grid, block, 0, s, a);
-    return hipGetLastError();
 }
 
 }  // namespace rs

@@ -356,12 +356,12 @@ struct ChunkBuilder {
         c.part = 0;
         c.nparts = 1;
         c.kind = KIND_SCALAR;
-        c.vpb_log2 = -1;
+        c.run_log2 = -1;
         out.push_back(c);
     }
 
     void vec(int64_t pos, int64_t blk, int64_t rows, int64_t cols, int64_t ld, int32_t part,
-             int32_t nparts, int32_t vpb_log2) {
+             int32_t nparts, int32_t run_log2) {
         ChunkDesc c{};
         c.pos = pos;
         c.blk = blk;
@@ -371,13 +371,13 @@ struct ChunkBuilder {
         c.part = part;
         c.nparts = nparts;
         c.kind = KIND_VEC;
-        c.vpb_log2 = vpb_log2;
+        c.run_log2 = run_log2;
         out.push_back(c);
     }
 
     // One contiguous block [s, s + n).
     void contiguous_block(int64_t s, int64_t n, int64_t blk) {
-        if (s % kVec != 0 || n % kVec != 0) {
+        if (s % kVecAlign != 0 || n % kVecAlign != 0) {
             scalar(s, blk, 1, n, n);
             return;
         }
@@ -407,7 +407,7 @@ struct ChunkBuilder {
                 c.part = 0;
                 c.nparts = 1;
                 c.kind = KIND_ELEM;
-                c.vpb_log2 = -1;
+                c.run_log2 = -1;
                 out.push_back(c);
                 i += len;
             }
@@ -421,10 +421,9 @@ struct ChunkBuilder {
             while (k < t.nblk) {
                 int64_t s = t.pos + k * t.u;
                 int64_t n = std::min(t.u, t.N - k * t.u);
-                int64_t vpb = n / kVec;
-                if (n == full && n % kVec == 0 && s % kVec == 0 && pow2(vpb) && vpb <= 64 &&
-                    n < CH) {
-                    // run of whole small blocks of one rank, handled by lane groups
+                if (n == full && s % kVecAlign == 0 && pow2(n) && n >= kVecAlign &&
+                    n <= (int64_t(1) << kMaxRunLog2) && n < CH) {
+                    // run of whole small blocks of one rank, reduced in lane groups
                     int32_t r = rank_of(s);
                     int64_t k1 = k + 1;
                     while (k1 < t.nblk && (k1 - k + 1) * n <= CH) {
@@ -432,7 +431,7 @@ struct ChunkBuilder {
                         if (std::min(t.u, t.N - k1 * t.u) != n || rank_of(s1) != r) break;
                         ++k1;
                     }
-                    vec(s, t.blk0 + k, 1, (k1 - k) * n, 0, 0, 1, ilog2(vpb));
+                    vec(s, t.blk0 + k, 1, (k1 - k) * n, 0, 0, 1, ilog2(n));
                     k = k1;
                     continue;
                 }
@@ -448,7 +447,10 @@ struct ChunkBuilder {
             int64_t r0 = bi * t.br, rows = std::min<int64_t>(t.br, t.R - r0);
             int64_t c0 = bj * t.bc, cols = std::min<int64_t>(t.bc, t.C - c0);
             int64_t s = t.pos + r0 * t.C + c0;
-            if (s % kVec != 0 || cols % kVec != 0 || t.C % kVec != 0 || cols > CH) {
+            // vector tiles address their elements with 32-bit offsets from the
+            // chunk start: rows * C must stay below 2^30
+            if (s % kVecAlign != 0 || cols % kVecAlign != 0 || t.C % kVecAlign != 0 || cols > CH ||
+                std::min<int64_t>(rows, CH / std::max<int64_t>(cols, 1)) * t.C >= (int64_t(1) << 30)) {
                 scalar(s, t.blk0 + k, rows, cols, t.C);
                 continue;
             }
@@ -488,11 +490,13 @@ rs_status build_tables(Plan& p, std::string& err) {
         }
         p.chunk_begin[size_t(k) * (m + 1) + m] = (int64_t)p.chunks.size();
     }
+    p.max_nparts = 1;
     for (const ChunkDesc& c : p.chunks) {
         if (c.nparts > 65535) {
             err = "a block needs more than 65535 chunks; raise the chunk size";
             return RS_EOVERFLOW;
         }
+        p.max_nparts = std::max(p.max_nparts, c.nparts);
     }
     // tensor tables in buffer order and the granule index
     const size_t n = p.t.size();

@@ -36,9 +36,10 @@ struct Plan {
     int64_t total = 0, nblocks = 0;
 
     // step work table (built for one chunk size)
-    int64_t chunk_elems = kMaxChunk;
+    int64_t chunk_elems = kDefaultChunk;
     bool tables_built = false;
     std::vector<ChunkDesc> chunks;
+    int32_t max_nparts = 1;            // most chunks any block is split into
     std::vector<int64_t> chunk_begin;  // [nb * (m + 1)]
     std::vector<int64_t> rank_blk;     // [nb * (m + 1)] first global block id per rank
     std::vector<int32_t> gidx;         // first tensor (buffer order) ending after granule start
@@ -53,7 +54,7 @@ struct Plan {
     void* d_ws = nullptr;
     bool uploaded = false, src_bound = false, dst_bound = false;
     bool src_vec = true, dst_vec = true;   // all views 16-byte aligned and starts % 8 == 0
-    int32_t split_mode = RS_SPLIT_TWO_PASS;
+    int32_t split_mode = RS_SPLIT_COOPERATIVE;
 
     int64_t cb(int32_t bucket, int32_t rank) const { return chunk_begin[size_t(bucket) * (m + 1) + rank]; }
 };

@@ -6,11 +6,14 @@
 namespace rs {
 
 // Work unit of the int8-AdamW kernel: what one workgroup updates.
-//   KIND_VEC    rows x cols elements (cols % 16 == 0, rows of stride ld, pos %
-//               16 == 0) handled as 16-element vectors, one per lane.
-//               vpb_log2 < 0: the chunk is part `part` of `nparts` of one
-//               block `blk`.  vpb_log2 >= 0: a contiguous run (rows == 1) of
-//               whole blocks of (1 << vpb_log2) vectors each, first block blk.
+//   KIND_VEC    rows x cols elements (cols % 4 == 0, rows of stride ld,
+//               pos % 4 == 0, ld % 4 == 0) handled as 4-element vectors:
+//               wave w covers chunk elements [1024 w, 1024 (w + 1)) as four
+//               256-element slices, lane l holding elements 256 k + 4 l .. +3.
+//               run_log2 < 0: the chunk is part `part` of `nparts` of one
+//               block `blk`.  run_log2 >= 0: a contiguous run (rows == 1) of
+//               whole blocks of (1 << run_log2) elements (4..256), first
+//               block blk.
 //   KIND_SCALAR one whole block of any shape/alignment (rows x cols, stride
 //               ld), element by element, two sweeps.
 //   KIND_ELEM   `cols` contiguous elements, each its own block (blk + i).
@@ -25,7 +28,7 @@ struct alignas(16) ChunkDesc {
     int32_t part;
     int32_t nparts;
     int32_t kind;
-    int32_t vpb_log2;
+    int32_t run_log2;
 };
 static_assert(sizeof(ChunkDesc) == 48, "ChunkDesc layout");
 
@@ -47,19 +50,19 @@ struct alignas(16) CoopSlot {
     uint32_t pad[2];
 };
 
-// Launch-wide counters of the cooperative step: chunk tickets handed out in
-// order and finished workgroups (the last one resets both).
+// Device status of the cooperative step.
 struct alignas(16) CoopCounters {
-    uint32_t ticket;
-    uint32_t done;
     uint32_t timeout;  // set when a bounded wait gave up
-    uint32_t pad;
+    uint32_t pad[3];
 };
 static_assert(sizeof(CoopSlot) == 32, "CoopSlot layout");
 
-constexpr int kVec = 16;             // elements per lane in the step kernel
-constexpr int kStepThreads = 1024;   // workgroup size of the step kernel
-constexpr int64_t kMaxChunk = int64_t(kVec) * kStepThreads;  // 16384
+constexpr int kVecAlign = 4;         // vector width (elements) of the step kernel
+constexpr int kElemsPerLane = 16;    // four 4-element vectors per lane
+constexpr int kMaxStepThreads = 1024;
+constexpr int64_t kMaxChunk = int64_t(kElemsPerLane) * kMaxStepThreads;  // 16384
+constexpr int kMaxRunLog2 = 8;       // small-block runs: blocks of 4..256 elements
+constexpr int64_t kDefaultChunk = 8192;
 constexpr int64_t kGranule = 65536;  // copy-kernel tensor-lookup granule
 constexpr int kL2Blocks = 2048;      // max partial sums of the L2 norm
 

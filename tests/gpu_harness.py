@@ -122,7 +122,7 @@ def assert_step_close(got: HostState, exp: HostState, mask: Optional[np.ndarray]
         assert np.allclose(a, b, rtol=1e-6, atol=0), f"{what}: {name}"
 
 
-def make_plan(specs, m, g_coll, chunk=None, mode=rs.RS_SPLIT_TWO_PASS) -> rs.Plan:
+def make_plan(specs, m, g_coll, chunk=None, mode=rs.RS_SPLIT_COOPERATIVE) -> rs.Plan:
     return rs.Plan(specs, m, g_coll, chunk=chunk, split_mode=mode).upload()
 
 
