@@ -15,9 +15,12 @@
 // in registers until the block absmax is known (wave butterfly, then LDS
 // across waves), so every byte is read once and written once.
 //
-// Arithmetic: the update follows the fixed binary32 order of the
-// definition with correctly rounded '/' and sqrt and no FMA contraction, so
-// m, v and the parameters match a correctly rounded evaluation bit for bit.
+// Arithmetic: the moments m, v follow the fixed binary32 order of the
+// definition with no FMA contraction, so they match a correctly rounded
+// evaluation bit for bit.  The parameter update uses the hardware square
+// root and reciprocal and falls back to correctly rounded operations where
+// that could leave the parameter tolerance (see param_fast); the scalar and
+// element paths use the correctly rounded operations throughout.
 // The quantisation ratio m / absmax is the correctly rounded quotient too,
 // formed from the block's correctly rounded reciprocal y and one residual
 // step q = q0 + (m - q0*a)*y with q0 = m*y (Markstein's correction): exact
@@ -130,6 +133,24 @@ __device__ __forceinline__ void moments(const StepScalars& sc, float g, float mh
 __device__ __forceinline__ float param(const StepScalars& sc, float theta, float m, float sq) {
     const float den = (sq * sc.kappa) + sc.eps;
     return (theta * sc.c_decay) - (sc.step_size * (m / den));
+}
+
+// The parameter update with the hardware square root and reciprocal (each
+// within 1 ulp): the update u then carries a relative error below 8 ulp
+// (4.8e-7) against the correctly rounded evaluation, and the new parameter
+// differs by at most 4.8e-7 |u| plus one rounding of each result.  That
+// stays inside |d| <= 1e-8 + 1e-6 |theta| whenever |u| <= 0.02 or
+// |theta_new| >= 0.6 |u|; otherwise (a large update cancelling most of the
+// parameter) `exact` is set and the caller recomputes with correctly rounded
+// operations.  No quantisation code depends on the parameter.
+__device__ __forceinline__ float param_fast(const StepScalars& sc, float theta, float m, float v,
+                                            bool& exact) {
+    const float den = (__builtin_amdgcn_sqrtf(v) * sc.kappa) + sc.eps;
+    const float u = sc.step_size * (m * __builtin_amdgcn_rcpf(den));
+    const float t = (theta * sc.c_decay) - u;
+    const float au = fabsf(u);
+    exact = exact || (au > 0.02f && fabsf(t) < 0.6f * au) || !(au <= 3.0e38f);
+    return t;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -382,9 +403,15 @@ __device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, floa
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             if (!act[k]) continue;
-            float t[4] = {TH[k].x, TH[k].y, TH[k].z, TH[k].w};
+            const float t0[4] = {TH[k].x, TH[k].y, TH[k].z, TH[k].w};
+            float t[4];
+            bool exact = false;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) t[j] = param(sc, t[j], M[4 * k + j], sqrtf(V[4 * k + j]));
+            for (int j = 0; j < 4; ++j) t[j] = param_fast(sc, t0[j], M[4 * k + j], V[4 * k + j], exact);
+            if (__builtin_expect(exact, 0)) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t[j] = param(sc, t0[j], M[4 * k + j], sqrtf(V[4 * k + j]));
+            }
             *reinterpret_cast<float4*>(th_b + p[k]) = make_float4(t[0], t[1], t[2], t[3]);
             if (out_b) {
                 const uint2 o = make_uint2(f32_to_bf16(t[0]) | (f32_to_bf16(t[1]) << 16),
