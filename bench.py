@@ -46,6 +46,24 @@ def algorithmic_bytes(plan, specs, total_blocks):
     }
 
 
+def recorded_traffic(workload: str):
+    """HBM bytes per step-kernel launch from the committed rocprofv3 counter
+    summary, only while the kernel source is the one that was profiled on
+    this workload (otherwise None)."""
+    import hashlib
+    rec = os.path.join(ROOT, "profiles", "adam8_step_traffic.json")
+    try:
+        with open(rec) as f:
+            r = json.load(f)
+        with open(os.path.join(ROOT, r["source"]), "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()
+    except (OSError, KeyError, ValueError):
+        return None
+    if not h.startswith(r["source_sha256_prefix"]) or r.get("workload_key") != workload:
+        return None
+    return r["hbm_bytes_per_launch"]
+
+
 def cpu_baseline(w, budget_s: float):
     """The oracle (single-threaded C) running the same hot path on a host
     copy of the same workload, repeated until budget_s is spent."""
@@ -254,7 +272,7 @@ def main():
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(step_gbs / PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": recorded_traffic(args.workload),
         },
         "event_ms_per_step": round(step_ms / args.steps, 5),
     }
