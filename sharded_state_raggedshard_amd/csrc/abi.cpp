@@ -434,7 +434,7 @@ rs_status rs_adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float
     b.out = d_bf16_out;
     b.chunks = reinterpret_cast<const rs::ChunkDesc*>(ws(p, p.off_chunks));
     b.cpart = reinterpret_cast<rs::ChunkPartial*>(ws(p, p.off_cpart));
-    b.coop = reinterpret_cast<rs::CoopSlot*>(ws(p, p.off_coop));
+    b.coop = reinterpret_cast<rs::PartSlot*>(ws(p, p.off_coop));
     b.counters = reinterpret_cast<rs::CoopCounters*>(ws(p, p.off_flag));
     for (const rs::Ranges& r : groups(chunk_ranges(p, bucket, rank))) {
         hipError_t e = rs::launch_adam8(r, b, sc, p.split_mode, p.chunk_elems, p.max_nparts,

@@ -137,20 +137,17 @@ __device__ __forceinline__ float param(const StepScalars& sc, float theta, float
 
 // The parameter update with the hardware square root and reciprocal (each
 // within 1 ulp): the update u then carries a relative error below 8 ulp
-// (4.8e-7) against the correctly rounded evaluation, and the new parameter
-// differs by at most 4.8e-7 |u| plus one rounding of each result.  That
-// stays inside |d| <= 1e-8 + 1e-6 |theta| whenever |u| <= 0.02 or
-// |theta_new| >= 0.6 |u|; otherwise (a large update cancelling most of the
-// parameter) `exact` is set and the caller recomputes with correctly rounded
-// operations.  No quantisation code depends on the parameter.
+// (4.8e-7) against the correctly rounded evaluation, so for |u| <= 0.02 the
+// new parameter differs by at most 9.6e-9 plus one rounding of the result,
+// inside |d| <= 1e-8 + 1e-6 |theta|.  Any other u (larger, infinite or NaN)
+// sets `exact` and the caller recomputes with correctly rounded operations.
+// No quantisation code depends on the parameter.
 __device__ __forceinline__ float param_fast(const StepScalars& sc, float theta, float m, float v,
                                             bool& exact) {
     const float den = (__builtin_amdgcn_sqrtf(v) * sc.kappa) + sc.eps;
     const float u = sc.step_size * (m * __builtin_amdgcn_rcpf(den));
-    const float t = (theta * sc.c_decay) - u;
-    const float au = fabsf(u);
-    exact = exact || (au > 0.02f && fabsf(t) < 0.6f * au) || !(au <= 3.0e38f);
-    return t;
+    exact = exact || !(fabsf(u) <= 0.02f);
+    return (theta * sc.c_decay) - u;
 }
 
 __device__ __forceinline__ float wave_max(float x) {
@@ -188,90 +185,84 @@ __device__ __forceinline__ int64_t chunk_of(const Ranges& r, int64_t wg) {
     return r.lo[i] + (wg - r.wg0[i]);
 }
 
-// The chunks of a split block meet through a slot of device-scope atomics
-// (the running maxima, the arrival count; a status word reports timeouts).
-// Agent-scope atomic loads read the coherent value, so no cache-wide
-// release / acquire is needed: the maxima are made complete before the
-// arrival is counted by waiting for the issuing wave's outstanding memory
-// operations, and the wait polls with relaxed loads (a release / acquire
-// pair would write back and invalidate the XCD's L2 on every arrival and
-// every poll).  coop_publish runs on thread 0 right after the chunk's
-// maxima are known; the parameter update runs before coop_wait, so the
-// other chunks' arrivals overlap with it.
+// The chunks of a split block meet through per-chunk slots (PartSlot).  A
+// chunk publishes its maxima with two relaxed device-scope 64-bit stores,
+// each carrying the sequence number of this call next to the value, so a
+// reader that sees the new sequence also sees that chunk's value and no
+// ordering between the two stores or against other memory is needed.
+// Device-scope atomics bypass the per-XCD L2, so every XCD sees the same
+// words.  Wave 0 of each chunk then polls the slots of all chunks of its
+// block with relaxed loads, one chunk per lane, until all show the
+// sequence, and reduces their maxima.
 
-struct CoopTicket {
-    uint64_t target;
-    int slot;
-};
-
-__device__ __forceinline__ CoopTicket coop_publish(const StepBuffers& B, const ChunkDesc& d,
-                                                   int64_t c, float am, float av) {
-    CoopSlot* cs = &B.coop[c - d.part];
-    const uint64_t np = (uint64_t)d.nparts;
-    const uint64_t a0 = __hip_atomic_load(&cs->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t gen = a0 / np;
-    const int slot = (int)(gen & 1u);
-    __hip_atomic_fetch_max(&cs->amax_m[slot], __float_as_uint(am), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_fetch_max(&cs->amax_v[slot], __float_as_uint(av), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&cs->amax_m[slot ^ 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&cs->amax_v[slot ^ 1], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_s_waitcnt(0);  // the maxima are performed before the arrival counts
-    __hip_atomic_fetch_add(&cs->arrive, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return CoopTicket{(gen + 1) * np, slot};
+__device__ __forceinline__ uint32_t coop_seq(const StepBuffers& B, int64_t c) {
+    const uint64_t w = __hip_atomic_load(&B.coop[c].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    return (uint32_t)(w >> 32) + 1u;
 }
 
-// Thread 0 waits for every chunk of the block (bounded) and returns the
-// block maxima.
-__device__ __forceinline__ void coop_wait(const StepBuffers& B, const ChunkDesc& d, int64_t c,
-                                          CoopTicket t, float& am, float& av) {
-    CoopSlot* cs = &B.coop[c - d.part];
+__device__ __forceinline__ void coop_publish(const StepBuffers& B, int64_t c, uint32_t seq,
+                                             float am, float av) {
+    const uint64_t hi = (uint64_t)seq << 32;
+    __hip_atomic_store(&B.coop[c].m, hi | __float_as_uint(am), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&B.coop[c].v, hi | __float_as_uint(av), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Run by all lanes of one wave: waits (bounded) until every chunk of the
+// block has published `seq`, and returns the block maxima in every lane.
+__device__ __forceinline__ void coop_wait(const StepBuffers& B, int64_t c0, int nparts,
+                                          uint32_t seq, float& am, float& av) {
+    const int lane = threadIdx.x & 63;
     uint32_t spins = 0;
-    while (__hip_atomic_load(&cs->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < t.target) {
+    for (;;) {
+        bool ok = true;
+        float xm = 0.0f, xv = 0.0f;
+        for (int q = lane; q < nparts; q += 64) {
+            const uint64_t wm =
+                __hip_atomic_load(&B.coop[c0 + q].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint64_t wv =
+                __hip_atomic_load(&B.coop[c0 + q].v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            ok = ok && (uint32_t)(wm >> 32) == seq && (uint32_t)(wv >> 32) == seq;
+            xm = fmaxf(xm, __uint_as_float((uint32_t)wm));
+            xv = fmaxf(xv, __uint_as_float((uint32_t)wv));
+        }
+        if (__all(ok)) {
+            am = wave_max(xm);
+            av = wave_max(xv);
+            return;
+        }
         __builtin_amdgcn_s_sleep(1);
         ++spins;
-        if ((spins & 255u) == 0 &&
-            __hip_atomic_load(&B.counters->timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0)
-            break;
-        if (spins > kSpinLimit) {
+        bool stop = spins > kSpinLimit;
+        if (stop && lane == 0)
             __hip_atomic_fetch_or(&B.counters->timeout, 1u, __ATOMIC_RELAXED,
                                   __HIP_MEMORY_SCOPE_AGENT);
-            break;
+        if ((spins & 255u) == 0)
+            stop = stop || __hip_atomic_load(&B.counters->timeout, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT) != 0;
+        if (__any(stop)) {
+            am = wave_max(xm);
+            av = wave_max(xv);
+            return;
         }
     }
-    am = __uint_as_float(
-        __hip_atomic_load(&cs->amax_m[t.slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
-    av = __uint_as_float(
-        __hip_atomic_load(&cs->amax_v[t.slot], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
 }
 
 // ------------------------------------------------------------ vector path
 
-template <int MODE, int NT, int KG>
-__device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, float s,
-                          const float* dqm, const float* dqv, float* red) {
-    constexpr int WSPAN = 256 * KG;  // chunk elements covered by one wave
-    const StepBuffers& B = a.b;
-    const StepScalars& sc = a.sc;
-    const bool split = d.nparts > 1;
-    if (MODE == MODE_PARTIAL && !split) return;
-    const bool run = d.run_log2 >= 0;
+// Lane element offsets of a vector chunk relative to d.pos: slice k of this
+// lane starts at chunk element e = WSPAN * wave + 256 k + 4 lane, which is
+// row e / cols, column e % cols of the chunk.
+template <int KG>
+__device__ __forceinline__ void lane_offsets(const ChunkDesc& d, uint32_t (&p)[KG],
+                                             bool (&act)[KG]) {
+    constexpr int WSPAN = 256 * KG;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = d.rows * d.cols;
     // row = e / cols via a multiply-high (exact for e, cols < 2^16)
     const uint32_t magic = d.rows > 1 ? (0xffffffffu / (uint32_t)d.cols) + 1u : 0u;
-
-    // Uniform chunk bases plus 32-bit lane offsets (tile chunks keep
-    // rows * ld < 2^30), so loads and stores use the scalar-base address mode.
-    float* __restrict__ th_b = B.theta + d.pos;
-    const uint16_t* __restrict__ g_b = B.grad + d.pos;
-    int8_t* __restrict__ qm_b = B.qm + d.pos;
-    uint8_t* __restrict__ qv_b = B.qv + d.pos;
-    uint16_t* __restrict__ out_b = B.out ? B.out + d.pos : nullptr;
-    uint32_t p[KG];
-    bool act[KG];
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
         const int e = wave * WSPAN + 256 * k + 4 * lane;
@@ -283,52 +274,105 @@ __device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, floa
             p[k] = row * (uint32_t)d.ld + ((uint32_t)e - row * (uint32_t)d.cols);
         }
     }
+}
 
-    // old absmax of the block(s) this lane touches
+// What a lane reads of one vector chunk: master, gradient and codes of its
+// 4 KG elements and the old absmax of the block(s) they belong to.
+template <int KG>
+struct VecIn {
+    float4 TH[KG];
+    uint2 GW[KG];
+    uint32_t CM[KG], CV[KG];
     float amo[KG], avo[KG];
+};
+
+// Issues every load of a vector chunk.  Tile chunks keep rows * ld < 2^30,
+// so a uniform chunk base plus 32-bit lane offsets addresses every element.
+template <int MODE, int KG>
+__device__ __forceinline__ void vec_load(const ChunkDesc& d, int64_t c, const StepBuffers& B,
+                                         VecIn<KG>& in) {
+    constexpr int WSPAN = 256 * KG;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint32_t p[KG];
+    bool act[KG];
+    lane_offsets<KG>(d, p, act);
+    const bool split = d.nparts > 1;
     if (MODE == MODE_MAIN && split) {
         const ChunkPartial cp = B.cpart[c];
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
-            amo[k] = cp.old_m;
-            avo[k] = cp.old_v;
+            in.amo[k] = cp.old_m;
+            in.avo[k] = cp.old_v;
         }
-    } else if (run) {
+    } else if (d.run_log2 >= 0) {
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             const int64_t blk = d.blk + ((wave * WSPAN + 256 * k + 4 * lane) >> d.run_log2);
-            amo[k] = act[k] ? B.amax_m[blk] : 0.0f;
-            avo[k] = act[k] ? B.amax_v[blk] : 0.0f;
+            in.amo[k] = act[k] ? B.amax_m[blk] : 0.0f;
+            in.avo[k] = act[k] ? B.amax_v[blk] : 0.0f;
         }
     } else {
         const float x = B.amax_m[d.blk], y = B.amax_v[d.blk];
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
-            amo[k] = x;
-            avo[k] = y;
+            in.amo[k] = x;
+            in.avo[k] = y;
         }
     }
-
-    // All loads first: the buffers may alias as far as the compiler knows, so
-    // without this each 4-element slice would wait for the previous slice's
-    // stores and a wave would pay four memory round trips instead of one.
-    float4 TH[KG];
-    uint2 GW[KG];
-    uint32_t CM[KG], CV[KG];
+    const float* th_b = B.theta + d.pos;
+    const uint16_t* g_b = B.grad + d.pos;
+    const int8_t* qm_b = B.qm + d.pos;
+    const uint8_t* qv_b = B.qv + d.pos;
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
+        uint2 gw = make_uint2(0u, 0u);
+        uint32_t cm = 0u, cv = 0u;
+        float4 th = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (act[k]) {
-            GW[k] = *reinterpret_cast<const uint2*>(g_b + p[k]);
-            CM[k] = *reinterpret_cast<const uint32_t*>(qm_b + p[k]);
-            CV[k] = *reinterpret_cast<const uint32_t*>(qv_b + p[k]);
-            TH[k] = MODE != MODE_PARTIAL ? *reinterpret_cast<const float4*>(th_b + p[k])
-                                         : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
-        } else {
-            GW[k] = make_uint2(0u, 0u);
-            CM[k] = CV[k] = 0u;
-            TH[k] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+            gw = *reinterpret_cast<const uint2*>(g_b + p[k]);
+            cm = *reinterpret_cast<const uint32_t*>(qm_b + p[k]);
+            cv = *reinterpret_cast<const uint32_t*>(qv_b + p[k]);
+            if (MODE != MODE_PARTIAL) th = *reinterpret_cast<const float4*>(th_b + p[k]);
         }
+        in.GW[k] = gw;
+        in.CM[k] = cm;
+        in.CV[k] = cv;
+        in.TH[k] = th;
     }
+}
+
+struct NoPrefetch {
+    __device__ __forceinline__ void operator()() const {}
+};
+
+// The update of one vector chunk from its loaded inputs.  `prefetch` runs
+// once the parameters are stored and before the wait for the other chunks
+// of a split block, so the next chunk's loads overlap that wait and the
+// quantisation.  redc holds the combined maxima of a cooperative block; it
+// is apart from red so that the next chunk's reduction cannot overwrite it
+// before every wave has read it.
+template <int MODE, int NT, int KG, class PF>
+__device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const StepArgs& a,
+                                            float s, const float* dqm, const float* dqv,
+                                            float* red, float* redc, const VecIn<KG>& in,
+                                            const PF& prefetch) {
+    constexpr int WSPAN = 256 * KG;
+    const StepBuffers& B = a.b;
+    const StepScalars& sc = a.sc;
+    const bool split = d.nparts > 1;
+    const bool run = d.run_log2 >= 0;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint32_t p[KG];
+    bool act[KG];
+    lane_offsets<KG>(d, p, act);
+    float* th_b = B.theta + d.pos;
+    int8_t* qm_b = B.qm + d.pos;
+    uint8_t* qv_b = B.qv + d.pos;
+    uint16_t* out_b = B.out ? B.out + d.pos : nullptr;
+    // sequence number this call publishes (cooperative split blocks)
+    const uint32_t seq = (MODE == MODE_COOP && split && wave == 0) ? coop_seq(B, c) : 0u;
 
     float M[4 * KG], V[4 * KG];
     float lm[KG], lv[KG];
@@ -336,12 +380,12 @@ __device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, floa
     for (int k = 0; k < KG; ++k) lm[k] = lv[k] = 0.0f;
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
-        const float g[4] = {bf16_lo(GW[k].x) * s, bf16_hi(GW[k].x) * s, bf16_lo(GW[k].y) * s,
-                            bf16_hi(GW[k].y) * s};
+        const float g[4] = {bf16_lo(in.GW[k].x) * s, bf16_hi(in.GW[k].x) * s,
+                            bf16_lo(in.GW[k].y) * s, bf16_hi(in.GW[k].y) * s};
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const float mh = dqm[(CM[k] >> (8 * j)) & 0xffu] * amo[k];
-            const float vh = dqv[(CV[k] >> (8 * j)) & 0xffu] * avo[k];
+            const float mh = dqm[(in.CM[k] >> (8 * j)) & 0xffu] * in.amo[k];
+            const float vh = dqv[(in.CV[k] >> (8 * j)) & 0xffu] * in.avo[k];
             moments(sc, g[j], mh, vh, M[4 * k + j], V[4 * k + j]);
             lm[k] = fmaxf(lm[k], fabsf(M[4 * k + j]));
             lv[k] = fmaxf(lv[k], V[4 * k + j]);
@@ -349,7 +393,6 @@ __device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, floa
     }
     // new absmax per block
     float am[KG], av[KG];
-    CoopTicket ticket{0, 0};
     bool wait = false;
     if (run) {
         // blocks of (1 << run_log2) elements = (1 << run_log2) / 4 lanes of one slice
@@ -385,10 +428,9 @@ __device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, floa
             wg_max2<NT>(x, y, red);
             if (split) {
                 if (MODE == MODE_PARTIAL) {
-                    if (threadIdx.x == 0) B.cpart[c] = ChunkPartial{x, y, amo[0], avo[0]};
+                    if (threadIdx.x == 0) B.cpart[c] = ChunkPartial{x, y, in.amo[0], in.avo[0]};
                     return;
                 }
-                if (threadIdx.x == 0) ticket = coop_publish(B, d, c, x, y);
                 wait = true;
             }
         }
@@ -399,18 +441,25 @@ __device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, floa
         }
     }
 
-    if (MODE != MODE_PARTIAL) {
+    // The parameter update needs no absmax.  In a cooperative split block,
+    // wave 0 first publishes and waits (its loads have all returned and it
+    // has no stores in flight, so nothing delays the polls), then updates
+    // its parameters after the barrier; the other waves update theirs while
+    // it waits.
+    auto params = [&]() {
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             if (!act[k]) continue;
-            const float t0[4] = {TH[k].x, TH[k].y, TH[k].z, TH[k].w};
+            const float t0[4] = {in.TH[k].x, in.TH[k].y, in.TH[k].z, in.TH[k].w};
             float t[4];
             bool exact = false;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) t[j] = param_fast(sc, t0[j], M[4 * k + j], V[4 * k + j], exact);
+            for (int j = 0; j < 4; ++j)
+                t[j] = param_fast(sc, t0[j], M[4 * k + j], V[4 * k + j], exact);
             if (__builtin_expect(exact, 0)) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) t[j] = param(sc, t0[j], M[4 * k + j], sqrtf(V[4 * k + j]));
+                for (int j = 0; j < 4; ++j)
+                    t[j] = param(sc, t0[j], M[4 * k + j], sqrtf(V[4 * k + j]));
             }
             *reinterpret_cast<float4*>(th_b + p[k]) = make_float4(t[0], t[1], t[2], t[3]);
             if (out_b) {
@@ -419,62 +468,78 @@ __device__ void vec_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, floa
                 *reinterpret_cast<uint2*>(out_b + p[k]) = o;
             }
         }
-    }
-
-    if (wait) {
-        // MODE_COOP, split block: the other chunks' maxima
-        if (threadIdx.x == 0) {
-            float x, y;
-            coop_wait(B, d, c, ticket, x, y);
-            red[0] = x;
-            red[1] = y;
+    };
+    const bool waiter = wait && wave == 0;
+    if (waiter) {
+        if (lane == 0) coop_publish(B, c, seq, am[0], av[0]);
+        float x, y;
+        coop_wait(B, c - d.part, d.nparts, seq, x, y);
+        if (lane == 0) {
+            redc[0] = x;
+            redc[1] = y;
         }
+    } else if (MODE != MODE_PARTIAL) {
+        params();
+    }
+    prefetch();
+    if (wait) {
         __syncthreads();
+        const float x = redc[0], y = redc[1];
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
-            am[k] = red[0];
-            av[k] = red[1];
+            am[k] = x;
+            av[k] = y;
         }
+        if (waiter) params();
     }
 
-#pragma unroll
-    for (int k = 0; k < KG; ++k) {
-        if (!act[k]) continue;
-        const float ym = quant_recip(am[k]), yv = quant_recip(av[k]);
+    // |m| <= absmax bounds the codes: no clamp; int8 via a +128 offset
+    auto quant = [&](int k, float a_m, float a_v, float ym, float yv) {
         uint32_t qmw = 0u, qvw = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            // |m| <= absmax bounds the codes: no clamp; int8 via a +128 offset
             qmw = __builtin_amdgcn_cvt_pk_u8_f32(
-                rintf(ratio_fast(M[4 * k + j], am[k], ym) * 127.0f) + 128.0f, j, qmw);
+                rintf(ratio_fast(M[4 * k + j], a_m, ym) * 127.0f) + 128.0f, j, qmw);
             qvw = __builtin_amdgcn_cvt_pk_u8_f32(
-                rintf(ratio_fast(V[4 * k + j], av[k], yv) * 255.0f), j, qvw);
+                rintf(ratio_fast(V[4 * k + j], a_v, yv) * 255.0f), j, qvw);
         }
         qmw ^= 0x80808080u;
-        if (__builtin_expect(quant_slow(am[k]) || quant_slow(av[k]), 0)) {
+        if (__builtin_expect(quant_slow(a_m) || quant_slow(a_v), 0)) {
             // absmax below 2^-60: plain division
             qmw = 0u;
             qvw = 0u;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                qmw |= code_m(M[4 * k + j], am[k], ym) << (8 * j);
-                qvw |= code_v(V[4 * k + j], av[k], yv) << (8 * j);
+                qmw |= code_m(M[4 * k + j], a_m, ym) << (8 * j);
+                qvw |= code_v(V[4 * k + j], a_v, yv) << (8 * j);
             }
         }
         *reinterpret_cast<uint32_t*>(qm_b + p[k]) = qmw;
         *reinterpret_cast<uint32_t*>(qv_b + p[k]) = qvw;
-        if (run) {
-            const int lanes = (1 << d.run_log2) >> 2;
+    };
+    if (run) {
+        const int lanes = (1 << d.run_log2) >> 2;
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            if (!act[k]) continue;
+            quant(k, am[k], av[k], quant_recip(am[k]), quant_recip(av[k]));
             if ((lane & (lanes - 1)) == 0) {
                 const int64_t blk = d.blk + ((wave * WSPAN + 256 * k + 4 * lane) >> d.run_log2);
                 B.amax_m[blk] = am[k];
                 B.amax_v[blk] = av[k];
             }
         }
-    }
-    if (!run && threadIdx.x == 0 && d.part == 0) {
-        B.amax_m[d.blk] = am[0];
-        B.amax_v[d.blk] = av[0];
+    } else {
+        // one block: one reciprocal per lane
+        const float a_m = am[0], a_v = av[0];
+        const float ym = quant_recip(a_m), yv = quant_recip(a_v);
+#pragma unroll
+        for (int k = 0; k < KG; ++k)
+            if (act[k]) quant(k, a_m, a_v, ym, yv);
+        if (threadIdx.x == 0 && d.part == 0) {
+            B.amax_m[d.blk] = a_m;
+            B.amax_v[d.blk] = a_v;
+        }
     }
 }
 
@@ -541,22 +606,33 @@ __device__ void elem_chunk(const ChunkDesc& d, const StepArgs& a, float s, const
     }
 }
 
-template <int MODE, int NT>
-__global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
-    __shared__ float dqm[256], dqv[256];
-    __shared__ float red[2 * (NT / 64) + 2];
-    // dequantisation tables: code -> code / 127 (int8), code / 255 (uint8)
+// Dequantisation tables: code -> code / 127 (int8), code / 255 (uint8).
+template <int NT>
+__device__ __forceinline__ void fill_tables(float* dqm, float* dqv) {
     for (int i = threadIdx.x; i < 256; i += NT) {
         dqm[i] = (float)(int8_t)(uint8_t)i / 127.0f;
         dqv[i] = (float)i / 255.0f;
     }
     __syncthreads();
-    const int64_t wg = blockIdx.x;
-    const int64_t c = chunk_of(a.r, wg);
+}
+
+// One workgroup per chunk.  MODE_PARTIAL and MODE_MAIN are the two launches
+// of the two-pass split; MODE_COOP combines split blocks inside one launch.
+template <int MODE, int NT>
+__global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
+    __shared__ float dqm[256], dqv[256];
+    __shared__ float red[2 * (NT / 64) + 2];
+    __shared__ float redc[2];
+    fill_tables<NT>(dqm, dqv);
+    const int64_t c = chunk_of(a.r, blockIdx.x);
     const ChunkDesc d = a.b.chunks[c];
+    // the partial pass only visits chunks of split blocks
+    if (MODE == MODE_PARTIAL && (d.kind != KIND_VEC || d.nparts == 1)) return;
     const float s = a.b.gscale ? *a.b.gscale : 1.0f;
     if (d.kind == KIND_VEC) {
-        vec_chunk<MODE, NT, kGroups>(d, c, a, s, dqm, dqv, red);
+        VecIn<kGroups> in;
+        vec_load<MODE, kGroups>(d, c, a.b, in);
+        vec_process<MODE, NT, kGroups>(d, c, a, s, dqm, dqv, red, redc, in, NoPrefetch{});
     } else if (MODE != MODE_PARTIAL) {
         if (d.kind == KIND_SCALAR)
             scalar_chunk<NT>(d, a, s, dqm, dqv, red);
@@ -565,7 +641,7 @@ __global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
     }
 }
 
-// Workgroups of one cooperative launch that are sure to be resident together.
+// Workgroups of the cooperative kernel that the device holds at once.
 template <int NT>
 int coop_capacity() {
     static std::mutex mu;
@@ -589,13 +665,16 @@ template <int NT>
 hipError_t launch_nt(const StepArgs& a, int32_t mode, int32_t max_nparts, hipStream_t s) {
     const dim3 grid((unsigned)a.nwg), block(NT);
     // cooperative only with a 2x margin on residency (other work may share the device)
-    if (mode == RS_SPLIT_COOPERATIVE && max_nparts > 1 && 2 * max_nparts <= coop_capacity<NT>()) {
+    if (mode == RS_SPLIT_COOPERATIVE && max_nparts > 1 &&
+        2 * (int64_t)max_nparts <= coop_capacity<NT>()) {
         hipLaunchKernelGGL((adam8_kernel<MODE_COOP, NT>), grid, block, 0, s, a);
         return hipGetLastError();
     }
-    hipLaunchKernelGGL((adam8_kernel<MODE_PARTIAL, NT>), grid, block, 0, s, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (max_nparts > 1) {
+        hipLaunchKernelGGL((adam8_kernel<MODE_PARTIAL, NT>), grid, block, 0, s, a);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     hipLaunchKernelGGL((adam8_kernel<MODE_MAIN, NT>), grid, block, 0, s, a);
     return hipGetLastError();
 }

@@ -63,7 +63,7 @@ struct StepBuffers {
     uint16_t* out;        // nullable
     const ChunkDesc* chunks;
     ChunkPartial* cpart;
-    CoopSlot* coop;
+    PartSlot* coop;
     CoopCounters* counters;
 };
 

@@ -533,7 +533,7 @@ rs_status build_tables(Plan& p, std::string& err) {
     p.off_cpart = off;
     off = align256(off + p.chunks.size() * sizeof(ChunkPartial));
     p.off_coop = off;
-    off = align256(off + p.chunks.size() * sizeof(CoopSlot));
+    off = align256(off + p.chunks.size() * sizeof(PartSlot));
     p.off_l2 = off;
     off = align256(off + size_t(kL2Blocks) * 8);
     p.off_flag = off;

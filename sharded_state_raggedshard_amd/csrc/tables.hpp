@@ -38,16 +38,14 @@ struct alignas(16) ChunkPartial {
     float pm, pv, old_m, old_v;
 };
 
-// Per-split-block scratch of the cooperative reduction, at the index of the
-// block's first chunk.  arrive counts part arrivals over all calls
-// (generation g = arrive / nparts, since every call adds exactly nparts);
-// amax_*[g & 1] holds the float bits of the running maxima of generation g,
-// and generation g clears the other slot for generation g + 1.
-struct alignas(16) CoopSlot {
-    uint64_t arrive;
-    uint32_t amax_m[2];
-    uint32_t amax_v[2];
-    uint32_t pad[2];
+// Per-chunk slot of the cooperative reduction: the chunk's partial maxima,
+// each as one 64-bit word (sequence << 32) | float bits.  Every call that
+// touches a split block updates all of its chunks, so the chunks of a block
+// always hold the same sequence; a call publishes sequence + 1 and waits
+// until every chunk of the block shows it.  Zeroed by the upload.
+struct alignas(16) PartSlot {
+    uint64_t m;
+    uint64_t v;
 };
 
 // Device status of the cooperative step.
@@ -55,7 +53,7 @@ struct alignas(16) CoopCounters {
     uint32_t timeout;  // set when a bounded wait gave up
     uint32_t pad[3];
 };
-static_assert(sizeof(CoopSlot) == 32, "CoopSlot layout");
+static_assert(sizeof(PartSlot) == 16, "PartSlot layout");
 
 constexpr int kVecAlign = 4;         // vector width (elements) of the step kernel
 constexpr int kElemsPerLane = 16;    // four 4-element vectors per lane
