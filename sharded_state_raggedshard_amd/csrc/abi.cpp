@@ -198,7 +198,7 @@ rs_status rs_plan_rank_blocks(const rs_plan* plan, int32_t bucket, int32_t rank,
 
 rs_status rs_plan_set_chunk(rs_plan* plan, int64_t chunk_elems) {
     if (!plan) return fail(RS_EINVAL, "plan is NULL");
-    if (chunk_elems < 64 || chunk_elems > rs::kMaxChunk || chunk_elems % rs::kElemsPerLane != 0)
+    if (chunk_elems < 64 || chunk_elems > rs::kMaxChunk || chunk_elems % rs::kChunkAlign != 0)
         return fail(RS_EINVAL, "chunk size must be a multiple of 16 in 64..16384");
     if (plan->p.uploaded) return fail(RS_ESTATE, "chunk size is fixed once the plan is uploaded");
     if (plan->p.chunk_elems != chunk_elems) {

@@ -7,13 +7,14 @@
 // int8 over 127 levels, v as uint8 over 255 levels) and the AdamW constants
 // are this library's definition; the pages do not fix them.
 //
-// One workgroup handles one chunk (<= 16 elements per thread).  Wave w of the
-// workgroup covers chunk elements [1024 w, 1024 w + 1024) as four 256-element
-// slices; lane l owns elements 256 k + 4 l .. +3 (k = 0..3), so each load and
-// store instruction of a wave touches one contiguous span (1 KiB of fp32,
-// 512 B of bf16, 256 B of codes).  The lane keeps its 16 new m and v values
-// in registers until the block absmax is known (wave butterfly, then LDS
-// across waves), so every byte is read once and written once.
+// One workgroup handles one chunk.  A lane owns 4 KG elements (KG = 4):
+// wave w of the workgroup covers chunk
+// elements [256 KG w, 256 KG (w + 1)) as KG 256-element slices, and lane l
+// owns elements 256 k + 4 l .. +3 of slice k, so each load and store
+// instruction of a wave touches one contiguous span (1 KiB of fp32, 512 B of
+// bf16, 256 B of codes).  The lane keeps its new m and v values in registers
+// until the block absmax is known (wave butterfly, then LDS across waves), so
+// every byte is read once and written once.
 //
 // Arithmetic: the moments m, v follow the fixed binary32 order of the
 // definition with no FMA contraction, so they match a correctly rounded
@@ -29,15 +30,18 @@
 //
 // Blocks larger than one chunk are split over several workgroups; their
 // absmax is combined either by a first launch that writes per-chunk partials
-// (two-pass) or inside one launch through device-scope counters
-// (cooperative).  In the cooperative launch the chunks of a block are
-// consecutive workgroups.  Workgroups are dispatched in index order on each
-// XCD, so a block's missing chunk can only be undispatched while its XCD is
-// full of workgroups whose indices lie inside that block's span; with P
-// chunks per block that needs more than P / 8 resident workgroups per XCD,
-// and the launch uses this mode only when the device holds twice the chunks
-// of the largest block.  Each wait is bounded and reports a timeout through
-// the device status word if it ever gives up.
+// (two-pass) or inside one launch (cooperative): every chunk publishes its
+// maxima into its own slot, tagged with a per-call sequence number, and every
+// wave then polls the slots of its block.  The chunks of a block are
+// consecutive workgroups, and workgroups are dispatched to the XCDs in turn
+// and in index order on each XCD.  A wait can only stall for good if some
+// workgroup w is never dispatched while every workgroup resident on its XCD
+// waits; each of those has already published and waits for a chunk at or
+// after w in its own block, so all of them have indices in (w - P, w) for a
+// block of P chunks, at most ceil(P / 8) of them per XCD.  The launch uses
+// this mode only when the device holds at least 2 P workgroups, far more
+// than 8 ceil(P / 8).  Each wait is bounded all the same and reports a
+// timeout through the device status word if it ever gives up.
 #include <hip/hip_runtime.h>
 
 #include <mutex>
@@ -51,8 +55,6 @@ namespace {
 
 enum { MODE_PARTIAL = 0, MODE_MAIN = 1, MODE_COOP = 2 };
 
-// 4-element groups per lane: a lane owns 4 * kGroups elements of its chunk.
-constexpr int kGroups = kElemsPerLane / 4;
 
 // Bounded wait for the other chunks of a block (tens of ms of sleeps; a
 // normal wait is microseconds).  After any timeout every later wait of the
@@ -276,6 +278,41 @@ __device__ __forceinline__ void lane_offsets(const ChunkDesc& d, uint32_t (&p)[K
     }
 }
 
+// Streaming accesses: every byte of the state is read once and written once
+// per step, so loads and stores carry the non-temporal hint.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float4 ld_f4(const float* p) {
+    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+    return make_float4(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z),
+                       __uint_as_float(t.w));
+}
+__device__ __forceinline__ uint2 ld_u2(const void* p) {
+    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+    return make_uint2(t.x, t.y);
+}
+__device__ __forceinline__ uint32_t ld_u1(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+}
+__device__ __forceinline__ void st_f4(float* p, float a, float b, float c, float d) {
+    u32x4 t;
+    t.x = __float_as_uint(a);
+    t.y = __float_as_uint(b);
+    t.z = __float_as_uint(c);
+    t.w = __float_as_uint(d);
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
+}
+__device__ __forceinline__ void st_u2(void* p, uint32_t a, uint32_t b) {
+    u32x2 t;
+    t.x = a;
+    t.y = b;
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
+}
+__device__ __forceinline__ void st_u1(void* p, uint32_t a) {
+    __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
+}
+
 // What a lane reads of one vector chunk: master, gradient and codes of its
 // 4 KG elements and the old absmax of the block(s) they belong to.
 template <int KG>
@@ -330,10 +367,10 @@ __device__ __forceinline__ void vec_load(const ChunkDesc& d, int64_t c, const St
         uint32_t cm = 0u, cv = 0u;
         float4 th = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
         if (act[k]) {
-            gw = *reinterpret_cast<const uint2*>(g_b + p[k]);
-            cm = *reinterpret_cast<const uint32_t*>(qm_b + p[k]);
-            cv = *reinterpret_cast<const uint32_t*>(qv_b + p[k]);
-            if (MODE != MODE_PARTIAL) th = *reinterpret_cast<const float4*>(th_b + p[k]);
+            gw = ld_u2(g_b + p[k]);
+            cm = ld_u1(qm_b + p[k]);
+            cv = ld_u1(qv_b + p[k]);
+            if (MODE != MODE_PARTIAL) th = ld_f4(th_b + p[k]);
         }
         in.GW[k] = gw;
         in.CM[k] = cm;
@@ -342,21 +379,11 @@ __device__ __forceinline__ void vec_load(const ChunkDesc& d, int64_t c, const St
     }
 }
 
-struct NoPrefetch {
-    __device__ __forceinline__ void operator()() const {}
-};
-
-// The update of one vector chunk from its loaded inputs.  `prefetch` runs
-// once the parameters are stored and before the wait for the other chunks
-// of a split block, so the next chunk's loads overlap that wait and the
-// quantisation.  redc holds the combined maxima of a cooperative block; it
-// is apart from red so that the next chunk's reduction cannot overwrite it
-// before every wave has read it.
-template <int MODE, int NT, int KG, class PF>
+// The update of one vector chunk from its loaded inputs.
+template <int MODE, int NT, int KG>
 __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const StepArgs& a,
                                             float s, const float* dqm, const float* dqv,
-                                            float* red, float* redc, const VecIn<KG>& in,
-                                            const PF& prefetch) {
+                                            float* red, const VecIn<KG>& in) {
     constexpr int WSPAN = 256 * KG;
     const StepBuffers& B = a.b;
     const StepScalars& sc = a.sc;
@@ -372,7 +399,7 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
     uint8_t* qv_b = B.qv + d.pos;
     uint16_t* out_b = B.out ? B.out + d.pos : nullptr;
     // sequence number this call publishes (cooperative split blocks)
-    const uint32_t seq = (MODE == MODE_COOP && split && wave == 0) ? coop_seq(B, c) : 0u;
+    const uint32_t seq = (MODE == MODE_COOP && split) ? coop_seq(B, c) : 0u;
 
     float M[4 * KG], V[4 * KG];
     float lm[KG], lv[KG];
@@ -441,11 +468,10 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
         }
     }
 
-    // The parameter update needs no absmax.  In a cooperative split block,
-    // wave 0 first publishes and waits (its loads have all returned and it
-    // has no stores in flight, so nothing delays the polls), then updates
-    // its parameters after the barrier; the other waves update theirs while
-    // it waits.
+    // The parameter update needs no absmax: in a cooperative split block
+    // thread 0 publishes the chunk's maxima, every wave updates its
+    // parameters and then polls the block's slots itself (no barrier), so
+    // the update overlaps the other chunks' progress.
     auto params = [&]() {
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
@@ -461,36 +487,22 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
                 for (int j = 0; j < 4; ++j)
                     t[j] = param(sc, t0[j], M[4 * k + j], sqrtf(V[4 * k + j]));
             }
-            *reinterpret_cast<float4*>(th_b + p[k]) = make_float4(t[0], t[1], t[2], t[3]);
-            if (out_b) {
-                const uint2 o = make_uint2(f32_to_bf16(t[0]) | (f32_to_bf16(t[1]) << 16),
-                                           f32_to_bf16(t[2]) | (f32_to_bf16(t[3]) << 16));
-                *reinterpret_cast<uint2*>(out_b + p[k]) = o;
-            }
+            st_f4(th_b + p[k], t[0], t[1], t[2], t[3]);
+            if (out_b)
+                st_u2(out_b + p[k], f32_to_bf16(t[0]) | (f32_to_bf16(t[1]) << 16),
+                      f32_to_bf16(t[2]) | (f32_to_bf16(t[3]) << 16));
         }
     };
-    const bool waiter = wait && wave == 0;
-    if (waiter) {
-        if (lane == 0) coop_publish(B, c, seq, am[0], av[0]);
+    if (wait && threadIdx.x == 0) coop_publish(B, c, seq, am[0], av[0]);
+    if (MODE != MODE_PARTIAL) params();
+    if (wait) {
         float x, y;
         coop_wait(B, c - d.part, d.nparts, seq, x, y);
-        if (lane == 0) {
-            redc[0] = x;
-            redc[1] = y;
-        }
-    } else if (MODE != MODE_PARTIAL) {
-        params();
-    }
-    prefetch();
-    if (wait) {
-        __syncthreads();
-        const float x = redc[0], y = redc[1];
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             am[k] = x;
             av[k] = y;
         }
-        if (waiter) params();
     }
 
     // |m| <= absmax bounds the codes: no clamp; int8 via a +128 offset
@@ -514,8 +526,8 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
                 qvw |= code_v(V[4 * k + j], a_v, yv) << (8 * j);
             }
         }
-        *reinterpret_cast<uint32_t*>(qm_b + p[k]) = qmw;
-        *reinterpret_cast<uint32_t*>(qv_b + p[k]) = qvw;
+        st_u1(qm_b + p[k], qmw);
+        st_u1(qv_b + p[k], qvw);
     };
     if (run) {
         const int lanes = (1 << d.run_log2) >> 2;
@@ -616,13 +628,13 @@ __device__ __forceinline__ void fill_tables(float* dqm, float* dqv) {
     __syncthreads();
 }
 
-// One workgroup per chunk.  MODE_PARTIAL and MODE_MAIN are the two launches
-// of the two-pass split; MODE_COOP combines split blocks inside one launch.
-template <int MODE, int NT>
+// One workgroup per chunk; each lane owns 4 KG elements (KG 4-element
+// groups).  MODE_PARTIAL and MODE_MAIN are the two launches of the two-pass
+// split; MODE_COOP combines split blocks inside one launch.
+template <int MODE, int NT, int KG>
 __global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
     __shared__ float dqm[256], dqv[256];
     __shared__ float red[2 * (NT / 64) + 2];
-    __shared__ float redc[2];
     fill_tables<NT>(dqm, dqv);
     const int64_t c = chunk_of(a.r, blockIdx.x);
     const ChunkDesc d = a.b.chunks[c];
@@ -630,9 +642,9 @@ __global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
     if (MODE == MODE_PARTIAL && (d.kind != KIND_VEC || d.nparts == 1)) return;
     const float s = a.b.gscale ? *a.b.gscale : 1.0f;
     if (d.kind == KIND_VEC) {
-        VecIn<kGroups> in;
-        vec_load<MODE, kGroups>(d, c, a.b, in);
-        vec_process<MODE, NT, kGroups>(d, c, a, s, dqm, dqv, red, redc, in, NoPrefetch{});
+        VecIn<KG> in;
+        vec_load<MODE, KG>(d, c, a.b, in);
+        vec_process<MODE, NT, KG>(d, c, a, s, dqm, dqv, red, in);
     } else if (MODE != MODE_PARTIAL) {
         if (d.kind == KIND_SCALAR)
             scalar_chunk<NT>(d, a, s, dqm, dqv, red);
@@ -642,7 +654,7 @@ __global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
 }
 
 // Workgroups of the cooperative kernel that the device holds at once.
-template <int NT>
+template <int NT, int KG>
 int coop_capacity() {
     static std::mutex mu;
     static int cached[64] = {0};
@@ -652,7 +664,7 @@ int coop_capacity() {
     if (cached[dev] == 0) {
         int per_cu = 0, ncu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(adam8_kernel<MODE_COOP, NT>), NT, 0) !=
+                &per_cu, reinterpret_cast<const void*>(adam8_kernel<MODE_COOP, NT, KG>), NT, 0) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -661,33 +673,35 @@ int coop_capacity() {
     return cached[dev];
 }
 
-template <int NT>
+template <int NT, int KG>
 hipError_t launch_nt(const StepArgs& a, int32_t mode, int32_t max_nparts, hipStream_t s) {
     const dim3 grid((unsigned)a.nwg), block(NT);
     // cooperative only with a 2x margin on residency (other work may share the device)
     if (mode == RS_SPLIT_COOPERATIVE && max_nparts > 1 &&
-        2 * (int64_t)max_nparts <= coop_capacity<NT>()) {
-        hipLaunchKernelGGL((adam8_kernel<MODE_COOP, NT>), grid, block, 0, s, a);
+        2 * (int64_t)max_nparts <= coop_capacity<NT, KG>()) {
+        hipLaunchKernelGGL((adam8_kernel<MODE_COOP, NT, KG>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     if (max_nparts > 1) {
-        hipLaunchKernelGGL((adam8_kernel<MODE_PARTIAL, NT>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((adam8_kernel<MODE_PARTIAL, NT, KG>), grid, block, 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((adam8_kernel<MODE_MAIN, NT>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((adam8_kernel<MODE_MAIN, NT, KG>), grid, block, 0, s, a);
     return hipGetLastError();
 }
 
 }  // namespace
 
-int step_threads(int64_t chunk_elems) {
-    const int64_t lanes = (chunk_elems + kElemsPerLane - 1) / kElemsPerLane;
-    if (lanes <= 64) return 64;
-    if (lanes <= 128) return 128;
-    if (lanes <= 256) return 256;
-    if (lanes <= 512) return 512;
-    return 1024;
+// Lanes own 16 elements: fewer, larger workgroups amortise the per-chunk
+// reduction and the cross-workgroup wait better than more waves with less
+// work each.
+StepGeometry step_geometry(int64_t chunk_elems) {
+    const int kg = 4;
+    const int64_t lanes = (chunk_elems + 4 * kg - 1) / (4 * kg);
+    int nt = 64;
+    while (nt < lanes && nt < kMaxStepThreads) nt *= 2;
+    return StepGeometry{nt, kg};
 }
 
 hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const StepScalars& sc,
@@ -705,17 +719,18 @@ hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const 
     a.nwg = total;
     if (total == 0) return hipSuccess;
     if (total > 0x7fffffffLL) return hipErrorInvalidValue;
-    switch (step_threads(chunk_elems)) {
+    const StepGeometry g = step_geometry(chunk_elems);
+    switch (g.threads) {
     case 64:
-        return launch_nt<64>(a, mode, max_nparts, s);
+        return launch_nt<64, 4>(a, mode, max_nparts, s);
     case 128:
-        return launch_nt<128>(a, mode, max_nparts, s);
+        return launch_nt<128, 4>(a, mode, max_nparts, s);
     case 256:
-        return launch_nt<256>(a, mode, max_nparts, s);
+        return launch_nt<256, 4>(a, mode, max_nparts, s);
     case 512:
-        return launch_nt<512>(a, mode, max_nparts, s);
+        return launch_nt<512, 4>(a, mode, max_nparts, s);
     default:
-        return launch_nt<1024>(a, mode, max_nparts, s);
+        return launch_nt<1024, 4>(a, mode, max_nparts, s);
     }
 }
 

@@ -73,7 +73,12 @@ struct StepBuffers {
 hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const StepScalars& sc,
                         int32_t mode, int64_t chunk_elems, int32_t max_nparts, hipStream_t s);
 
-// Workgroup size the step kernel uses for a chunk size.
-int step_threads(int64_t chunk_elems);
+// Workgroup size and 4-element groups per lane of the step kernel for a
+// chunk size.
+struct StepGeometry {
+    int threads;
+    int kg;
+};
+StepGeometry step_geometry(int64_t chunk_elems);
 
 }  // namespace rs

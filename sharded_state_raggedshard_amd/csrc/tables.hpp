@@ -8,8 +8,9 @@ namespace rs {
 // Work unit of the int8-AdamW kernel: what one workgroup updates.
 //   KIND_VEC    rows x cols elements (cols % 4 == 0, rows of stride ld,
 //               pos % 4 == 0, ld % 4 == 0) handled as 4-element vectors:
-//               wave w covers chunk elements [1024 w, 1024 (w + 1)) as four
-//               256-element slices, lane l holding elements 256 k + 4 l .. +3.
+//               with KG 4-element groups per lane, wave w covers chunk
+//               elements [256 KG w, 256 KG (w + 1)) as KG 256-element
+//               slices, lane l holding elements 256 k + 4 l .. +3.
 //               run_log2 < 0: the chunk is part `part` of `nparts` of one
 //               block `blk`.  run_log2 >= 0: a contiguous run (rows == 1) of
 //               whole blocks of (1 << run_log2) elements (4..256), first
@@ -56,9 +57,9 @@ struct alignas(16) CoopCounters {
 static_assert(sizeof(PartSlot) == 16, "PartSlot layout");
 
 constexpr int kVecAlign = 4;         // vector width (elements) of the step kernel
-constexpr int kElemsPerLane = 16;    // four 4-element vectors per lane
+constexpr int kChunkAlign = 16;      // chunk sizes are multiples of 16 elements
 constexpr int kMaxStepThreads = 1024;
-constexpr int64_t kMaxChunk = int64_t(kElemsPerLane) * kMaxStepThreads;  // 16384
+constexpr int64_t kMaxChunk = int64_t(16) * kMaxStepThreads;  // 16 elements per lane at most
 constexpr int kMaxRunLog2 = 8;       // small-block runs: blocks of 4..256 elements
 constexpr int64_t kDefaultChunk = 8192;
 constexpr int64_t kGranule = 65536;  // copy-kernel tensor-lookup granule
