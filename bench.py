@@ -260,7 +260,7 @@ def main():
             "padding": plan.padding[0],
             "quant_blocks": nblk,
             "split_mode": args.split_mode,
-            "chunk_elems": args.chunk or 8192,
+            "chunk_elems": rs.rs_plan_chunk_elems(plan.h),
             "planner_s": round(plan_s, 4),
         },
         "step_params_per_s": round(real / (per_op["adam8_step"] * 1e-3), 1),

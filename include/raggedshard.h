@@ -138,8 +138,10 @@ rs_status rs_plan_rank_blocks(const rs_plan* plan, int32_t bucket, int32_t rank,
                               int64_t* count);
 
 /* Maximum elements one workgroup handles in the step (a multiple of 16 in
- * 64..16384, default 8192).  Larger blocks are split into chunks.  Must be
- * called before rs_plan_upload.  Errors: RS_EINVAL, RS_ESTATE (uploaded). */
+ * 64..16384).  Larger blocks are split into chunks.  The planner's default
+ * is 8192, or 4096 when most elements sit in tiles narrower than their
+ * tensor.  Must be called before rs_plan_upload.  Errors: RS_EINVAL,
+ * RS_ESTATE (uploaded). */
 rs_status rs_plan_set_chunk(rs_plan* plan, int64_t chunk_elems);
 
 /* RS_SPLIT_COOPERATIVE (default) or RS_SPLIT_TWO_PASS; may change at any
@@ -148,9 +150,9 @@ rs_status rs_plan_set_chunk(rs_plan* plan, int64_t chunk_elems);
  * (occupancy of the step kernel times the compute units). */
 rs_status rs_plan_set_split_mode(rs_plan* plan, int32_t mode);
 
-/* Number of chunks of the step's work table (valid after the chunk size is
- * fixed; for sizing and reporting). */
-rs_status rs_plan_chunk_count(const rs_plan* plan, int64_t* n_chunks);
+/* Number of chunks of the step's work table and the chunk size in effect
+ * (for sizing and reporting).  Either output pointer may be NULL. */
+rs_status rs_plan_chunk_count(const rs_plan* plan, int64_t* n_chunks, int64_t* chunk_elems);
 
 /* Device bytes the workspace must provide (tables + scratch). */
 size_t rs_plan_device_bytes(const rs_plan* plan);

@@ -75,7 +75,7 @@ def lib() -> C.CDLL:
         "rs_plan_rank_blocks": ([vp, i32, i32, P64, P64], C.c_int),
         "rs_plan_set_chunk": ([vp, i64], C.c_int),
         "rs_plan_set_split_mode": ([vp, i32], C.c_int),
-        "rs_plan_chunk_count": ([vp, P64], C.c_int),
+        "rs_plan_chunk_count": ([vp, P64, P64], C.c_int),
         "rs_plan_device_bytes": ([vp], C.c_size_t),
         "rs_plan_upload": ([vp, vp, C.c_size_t, vp], C.c_int),
         "rs_bind_views": ([vp, i32, C.POINTER(vp), vp], C.c_int),
@@ -192,8 +192,15 @@ def rs_plan_set_split_mode(plan: int, mode: int) -> None:
 
 def rs_plan_chunk_count(plan: int) -> int:
     n = C.c_int64()
-    _check(lib().rs_plan_chunk_count(plan, C.byref(n)))
+    _check(lib().rs_plan_chunk_count(plan, C.byref(n), None))
     return n.value
+
+
+def rs_plan_chunk_elems(plan: int) -> int:
+    """Chunk size (elements per step workgroup) in effect for the plan."""
+    c = C.c_int64()
+    _check(lib().rs_plan_chunk_count(plan, None, C.byref(c)))
+    return c.value
 
 
 def rs_plan_device_bytes(plan: int) -> int:

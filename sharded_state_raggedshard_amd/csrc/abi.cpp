@@ -216,12 +216,13 @@ rs_status rs_plan_set_split_mode(rs_plan* plan, int32_t mode) {
     return RS_OK;
 }
 
-rs_status rs_plan_chunk_count(const rs_plan* plan, int64_t* n_chunks) {
-    if (!plan || !n_chunks) return fail(RS_EINVAL, "NULL argument");
+rs_status rs_plan_chunk_count(const rs_plan* plan, int64_t* n_chunks, int64_t* chunk_elems) {
+    if (!plan) return fail(RS_EINVAL, "NULL argument");
     rs::Plan& p = const_cast<rs_plan*>(plan)->p;
     rs_status st = ensure_tables(p);
     if (st != RS_OK) return st;
-    *n_chunks = (int64_t)p.chunks.size();
+    if (n_chunks) *n_chunks = (int64_t)p.chunks.size();
+    if (chunk_elems) *chunk_elems = p.chunk_elems;
     return RS_OK;
 }
 

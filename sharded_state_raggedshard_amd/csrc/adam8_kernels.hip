@@ -65,7 +65,7 @@ struct StepArgs {
     Ranges r;  // chunk-index ranges; wg0 = prefix counts
     StepBuffers b;
     StepScalars sc;
-    int64_t nwg;
+    int64_t nwg;  // chunks of the launch (linear indices 0 .. nwg - 1)
 };
 
 __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
@@ -379,29 +379,28 @@ __device__ __forceinline__ void vec_load(const ChunkDesc& d, int64_t c, const St
     }
 }
 
-// The update of one vector chunk from its loaded inputs.
+// What the phases of one vector chunk carry between them.
+template <int KG>
+struct VecState {
+    float M[4 * KG], V[4 * KG];  // new moments of this lane's elements
+    float am[KG], av[KG];        // new absmax of the block(s) of each slice
+    uint32_t seq;                // sequence number published (cooperative split)
+    bool wait;                   // the block's other chunks must be waited for
+};
+
+// Front: moments and the new block maxima; a cooperative split chunk
+// publishes its maxima.  Returns false when nothing is left to do (the
+// partial pass of a split chunk).
 template <int MODE, int NT, int KG>
-__device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const StepArgs& a,
-                                            float s, const float* dqm, const float* dqv,
-                                            float* red, const VecIn<KG>& in) {
-    constexpr int WSPAN = 256 * KG;
+__device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const StepArgs& a,
+                                          float s, const float* dqm, const float* dqv,
+                                          float* red, const VecIn<KG>& in, VecState<KG>& st) {
     const StepBuffers& B = a.b;
     const StepScalars& sc = a.sc;
     const bool split = d.nparts > 1;
-    const bool run = d.run_log2 >= 0;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    uint32_t p[KG];
-    bool act[KG];
-    lane_offsets<KG>(d, p, act);
-    float* th_b = B.theta + d.pos;
-    int8_t* qm_b = B.qm + d.pos;
-    uint8_t* qv_b = B.qv + d.pos;
-    uint16_t* out_b = B.out ? B.out + d.pos : nullptr;
     // sequence number this call publishes (cooperative split blocks)
-    const uint32_t seq = (MODE == MODE_COOP && split) ? coop_seq(B, c) : 0u;
-
-    float M[4 * KG], V[4 * KG];
+    st.seq = (MODE == MODE_COOP && split) ? coop_seq(B, c) : 0u;
+    st.wait = false;
     float lm[KG], lv[KG];
 #pragma unroll
     for (int k = 0; k < KG; ++k) lm[k] = lv[k] = 0.0f;
@@ -413,107 +412,124 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
         for (int j = 0; j < 4; ++j) {
             const float mh = dqm[(in.CM[k] >> (8 * j)) & 0xffu] * in.amo[k];
             const float vh = dqv[(in.CV[k] >> (8 * j)) & 0xffu] * in.avo[k];
-            moments(sc, g[j], mh, vh, M[4 * k + j], V[4 * k + j]);
-            lm[k] = fmaxf(lm[k], fabsf(M[4 * k + j]));
-            lv[k] = fmaxf(lv[k], V[4 * k + j]);
+            moments(sc, g[j], mh, vh, st.M[4 * k + j], st.V[4 * k + j]);
+            lm[k] = fmaxf(lm[k], fabsf(st.M[4 * k + j]));
+            lv[k] = fmaxf(lv[k], st.V[4 * k + j]);
         }
     }
-    // new absmax per block
-    float am[KG], av[KG];
-    bool wait = false;
-    if (run) {
+    if (d.run_log2 >= 0) {
         // blocks of (1 << run_log2) elements = (1 << run_log2) / 4 lanes of one slice
         const int lanes = (1 << d.run_log2) >> 2;
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
-            am[k] = lm[k];
-            av[k] = lv[k];
+            st.am[k] = lm[k];
+            st.av[k] = lv[k];
             for (int off = 1; off < lanes; off <<= 1) {
-                am[k] = fmaxf(am[k], __shfl_xor(am[k], off, 64));
-                av[k] = fmaxf(av[k], __shfl_xor(av[k], off, 64));
+                st.am[k] = fmaxf(st.am[k], __shfl_xor(st.am[k], off, 64));
+                st.av[k] = fmaxf(st.av[k], __shfl_xor(st.av[k], off, 64));
             }
+        }
+        return true;
+    }
+    float x, y;
+    if (MODE == MODE_MAIN && split) {
+        x = 0.0f;
+        y = 0.0f;
+        const int64_t c0 = c - d.part;
+        for (int q = 0; q < d.nparts; ++q) {
+            const ChunkPartial cp = B.cpart[c0 + q];
+            x = fmaxf(x, cp.pm);
+            y = fmaxf(y, cp.pv);
         }
     } else {
-        float x, y;
-        if (MODE == MODE_MAIN && split) {
-            x = 0.0f;
-            y = 0.0f;
-            const int64_t c0 = c - d.part;
-            for (int q = 0; q < d.nparts; ++q) {
-                const ChunkPartial cp = B.cpart[c0 + q];
-                x = fmaxf(x, cp.pm);
-                y = fmaxf(y, cp.pv);
-            }
-        } else {
-            x = lm[0];
-            y = lv[0];
+        x = lm[0];
+        y = lv[0];
 #pragma unroll
-            for (int k = 1; k < KG; ++k) {
-                x = fmaxf(x, lm[k]);
-                y = fmaxf(y, lv[k]);
-            }
-            wg_max2<NT>(x, y, red);
-            if (split) {
-                if (MODE == MODE_PARTIAL) {
-                    if (threadIdx.x == 0) B.cpart[c] = ChunkPartial{x, y, in.amo[0], in.avo[0]};
-                    return;
-                }
-                wait = true;
-            }
+        for (int k = 1; k < KG; ++k) {
+            x = fmaxf(x, lm[k]);
+            y = fmaxf(y, lv[k]);
         }
-#pragma unroll
-        for (int k = 0; k < KG; ++k) {
-            am[k] = x;
-            av[k] = y;
+        wg_max2<NT>(x, y, red);
+        if (split) {
+            if (MODE == MODE_PARTIAL) {
+                if (threadIdx.x == 0) B.cpart[c] = ChunkPartial{x, y, in.amo[0], in.avo[0]};
+                return false;
+            }
+            st.wait = true;
+            if (threadIdx.x == 0) coop_publish(B, c, st.seq, x, y);
         }
     }
-
-    // The parameter update needs no absmax: in a cooperative split block
-    // thread 0 publishes the chunk's maxima, every wave updates its
-    // parameters and then polls the block's slots itself (no barrier), so
-    // the update overlaps the other chunks' progress.
-    auto params = [&]() {
 #pragma unroll
-        for (int k = 0; k < KG; ++k) {
-            if (!act[k]) continue;
-            const float t0[4] = {in.TH[k].x, in.TH[k].y, in.TH[k].z, in.TH[k].w};
-            float t[4];
-            bool exact = false;
+    for (int k = 0; k < KG; ++k) {
+        st.am[k] = x;
+        st.av[k] = y;
+    }
+    return true;
+}
+
+// Parameters: needs no absmax, so it runs before any wait.
+template <int KG>
+__device__ __forceinline__ void vec_params(const ChunkDesc& d, const StepArgs& a,
+                                           const VecIn<KG>& in, const VecState<KG>& st) {
+    const StepScalars& sc = a.sc;
+    uint32_t p[KG];
+    bool act[KG];
+    lane_offsets<KG>(d, p, act);
+    float* th_b = a.b.theta + d.pos;
+    uint16_t* out_b = a.b.out ? a.b.out + d.pos : nullptr;
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+        if (!act[k]) continue;
+        const float t0[4] = {in.TH[k].x, in.TH[k].y, in.TH[k].z, in.TH[k].w};
+        float t[4];
+        bool exact = false;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            t[j] = param_fast(sc, t0[j], st.M[4 * k + j], st.V[4 * k + j], exact);
+        if (__builtin_expect(exact, 0)) {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                t[j] = param_fast(sc, t0[j], M[4 * k + j], V[4 * k + j], exact);
-            if (__builtin_expect(exact, 0)) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    t[j] = param(sc, t0[j], M[4 * k + j], sqrtf(V[4 * k + j]));
-            }
-            st_f4(th_b + p[k], t[0], t[1], t[2], t[3]);
-            if (out_b)
-                st_u2(out_b + p[k], f32_to_bf16(t[0]) | (f32_to_bf16(t[1]) << 16),
-                      f32_to_bf16(t[2]) | (f32_to_bf16(t[3]) << 16));
+                t[j] = param(sc, t0[j], st.M[4 * k + j], sqrtf(st.V[4 * k + j]));
         }
-    };
-    if (wait && threadIdx.x == 0) coop_publish(B, c, seq, am[0], av[0]);
-    if (MODE != MODE_PARTIAL) params();
-    if (wait) {
+        st_f4(th_b + p[k], t[0], t[1], t[2], t[3]);
+        if (out_b)
+            st_u2(out_b + p[k], f32_to_bf16(t[0]) | (f32_to_bf16(t[1]) << 16),
+                  f32_to_bf16(t[2]) | (f32_to_bf16(t[3]) << 16));
+    }
+}
+
+// Back: waits for the block's other chunks if needed (every wave polls the
+// slots itself, no barrier), then quantises and stores codes and absmax.
+template <int KG>
+__device__ __forceinline__ void vec_back(const ChunkDesc& d, int64_t c, const StepArgs& a,
+                                         VecState<KG>& st) {
+    constexpr int WSPAN = 256 * KG;
+    const StepBuffers& B = a.b;
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint32_t p[KG];
+    bool act[KG];
+    lane_offsets<KG>(d, p, act);
+    int8_t* qm_b = B.qm + d.pos;
+    uint8_t* qv_b = B.qv + d.pos;
+    if (st.wait) {
         float x, y;
-        coop_wait(B, c - d.part, d.nparts, seq, x, y);
+        coop_wait(B, c - d.part, d.nparts, st.seq, x, y);
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
-            am[k] = x;
-            av[k] = y;
+            st.am[k] = x;
+            st.av[k] = y;
         }
     }
-
     // |m| <= absmax bounds the codes: no clamp; int8 via a +128 offset
     auto quant = [&](int k, float a_m, float a_v, float ym, float yv) {
         uint32_t qmw = 0u, qvw = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             qmw = __builtin_amdgcn_cvt_pk_u8_f32(
-                rintf(ratio_fast(M[4 * k + j], a_m, ym) * 127.0f) + 128.0f, j, qmw);
+                rintf(ratio_fast(st.M[4 * k + j], a_m, ym) * 127.0f) + 128.0f, j, qmw);
             qvw = __builtin_amdgcn_cvt_pk_u8_f32(
-                rintf(ratio_fast(V[4 * k + j], a_v, yv) * 255.0f), j, qvw);
+                rintf(ratio_fast(st.V[4 * k + j], a_v, yv) * 255.0f), j, qvw);
         }
         qmw ^= 0x80808080u;
         if (__builtin_expect(quant_slow(a_m) || quant_slow(a_v), 0)) {
@@ -522,28 +538,28 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
             qvw = 0u;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                qmw |= code_m(M[4 * k + j], a_m, ym) << (8 * j);
-                qvw |= code_v(V[4 * k + j], a_v, yv) << (8 * j);
+                qmw |= code_m(st.M[4 * k + j], a_m, ym) << (8 * j);
+                qvw |= code_v(st.V[4 * k + j], a_v, yv) << (8 * j);
             }
         }
         st_u1(qm_b + p[k], qmw);
         st_u1(qv_b + p[k], qvw);
     };
-    if (run) {
+    if (d.run_log2 >= 0) {
         const int lanes = (1 << d.run_log2) >> 2;
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             if (!act[k]) continue;
-            quant(k, am[k], av[k], quant_recip(am[k]), quant_recip(av[k]));
+            quant(k, st.am[k], st.av[k], quant_recip(st.am[k]), quant_recip(st.av[k]));
             if ((lane & (lanes - 1)) == 0) {
                 const int64_t blk = d.blk + ((wave * WSPAN + 256 * k + 4 * lane) >> d.run_log2);
-                B.amax_m[blk] = am[k];
-                B.amax_v[blk] = av[k];
+                B.amax_m[blk] = st.am[k];
+                B.amax_v[blk] = st.av[k];
             }
         }
     } else {
         // one block: one reciprocal per lane
-        const float a_m = am[0], a_v = av[0];
+        const float a_m = st.am[0], a_v = st.av[0];
         const float ym = quant_recip(a_m), yv = quant_recip(a_v);
 #pragma unroll
         for (int k = 0; k < KG; ++k)
@@ -553,6 +569,17 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
             B.amax_v[d.blk] = a_v;
         }
     }
+}
+
+// The whole update of one vector chunk from its loaded inputs.
+template <int MODE, int NT, int KG>
+__device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const StepArgs& a,
+                                            float s, const float* dqm, const float* dqv,
+                                            float* red, const VecIn<KG>& in) {
+    VecState<KG> st;
+    if (!vec_front<MODE, NT, KG>(d, c, a, s, dqm, dqv, red, in, st)) return;
+    if (MODE != MODE_PARTIAL) vec_params<KG>(d, a, in, st);
+    vec_back<KG>(d, c, a, st);
 }
 
 // --------------------------------------------------- generic block paths
@@ -628,19 +655,12 @@ __device__ __forceinline__ void fill_tables(float* dqm, float* dqv) {
     __syncthreads();
 }
 
-// One workgroup per chunk; each lane owns 4 KG elements (KG 4-element
-// groups).  MODE_PARTIAL and MODE_MAIN are the two launches of the two-pass
-// split; MODE_COOP combines split blocks inside one launch.
+// One chunk, start to end.
 template <int MODE, int NT, int KG>
-__global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
-    __shared__ float dqm[256], dqv[256];
-    __shared__ float red[2 * (NT / 64) + 2];
-    fill_tables<NT>(dqm, dqv);
-    const int64_t c = chunk_of(a.r, blockIdx.x);
-    const ChunkDesc d = a.b.chunks[c];
+__device__ __forceinline__ void one_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, float s,
+                                          const float* dqm, const float* dqv, float* red) {
     // the partial pass only visits chunks of split blocks
     if (MODE == MODE_PARTIAL && (d.kind != KIND_VEC || d.nparts == 1)) return;
-    const float s = a.b.gscale ? *a.b.gscale : 1.0f;
     if (d.kind == KIND_VEC) {
         VecIn<KG> in;
         vec_load<MODE, KG>(d, c, a.b, in);
@@ -651,6 +671,20 @@ __global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
         else
             elem_chunk<NT>(d, a, s, dqm, dqv);
     }
+}
+
+// One workgroup per chunk; each lane owns 4 KG elements (KG 4-element
+// groups).  MODE_PARTIAL and MODE_MAIN are the two launches of the two-pass
+// split; MODE_COOP combines split blocks inside one launch.
+template <int MODE, int NT, int KG>
+__global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
+    __shared__ float dqm[256], dqv[256];
+    __shared__ float red[2 * (NT / 64) + 2];
+    fill_tables<NT>(dqm, dqv);
+    const int64_t c = chunk_of(a.r, blockIdx.x);
+    const ChunkDesc d = a.b.chunks[c];
+    const float s = a.b.gscale ? *a.b.gscale : 1.0f;
+    one_chunk<MODE, NT, KG>(d, c, a, s, dqm, dqv, red);
 }
 
 // Workgroups of the cooperative kernel that the device holds at once.
