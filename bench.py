@@ -5,12 +5,20 @@ gradients, in stream order on one GPU:
     group_l2norm(grad, all slices) -> clip_coef -> adam8_step(all slices,
     grad scale = clip coefficient) -> pack_shard(all slices, fp32 master ->
     bf16 gathered buffer) -> unpack_full(bf16 buffer -> per-parameter views)
-    -> group_zero(grad)
+    -> group_zero(the gradient accumulation buffer of the next step)
 All m simulated ranks' slices live in one device buffer (the gathered
-buffer stands in for AllGather / ReduceScatter).  Inputs are resident in
-HBM before the timed region.  Prints one JSON line.
+buffer stands in for AllGather / ReduceScatter).  Two seeded random
+gradient buffers alternate between steps, so every step reads a full
+synthetic gradient; the zeroing clears a third buffer of the same size (what
+the next backward pass would accumulate into).  Inputs are resident in HBM
+before the timed region.  Prints one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama_layer]
+With --rank R the l2norm, the step, the pack and the zeroing act on rank R's
+slices of every bucket (its ragged local shard: the per-rank work of one
+GPU in an m-GPU job), and the copy-out unpacks bucket 0 (one gathered
+bucket).  No CPU baseline is run in that mode.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama_layer] [--rank R]
 """
 from __future__ import annotations
 
@@ -27,10 +35,27 @@ METRIC = "int8-AdamW shard step params/s + HBM GB/s (% peak); pack/unpack GB/s"
 PEAK_GBS = 8000.0  # MI355X HBM3E
 
 
-def algorithmic_bytes(plan, specs, total_blocks):
+def selection_sizes(plan, specs, rank):
+    """(real elements, buffer elements, quantisation blocks) of the selected
+    slices: everything, or rank `rank`'s slice of every bucket."""
+    import sharded_state_raggedshard_amd as rs
+
+    if rank is None:
+        return sum(s.numel for s in specs), plan.total, plan.n_blocks
+    real = buf = blocks = 0
+    for b in range(plan.nb):
+        lo = plan.base[b] + rank * plan.S[b]
+        hi = lo + plan.S[b]
+        buf += plan.S[b]
+        blocks += rs.rs_plan_rank_blocks(plan.h, b, rank)[1]
+        for i, s in enumerate(specs):
+            if int(getattr(s, "bucket", 0)) == b:
+                real += max(0, min(hi, plan.pos[i] + s.numel) - max(lo, plan.pos[i]))
+    return real, buf, blocks
+
+
+def algorithmic_bytes(real, buf, total_blocks, unpack_real):
     """Bytes each op must move (not counting padding the op never touches)."""
-    real = sum(s.numel for s in specs)
-    buf = plan.total
     pad = buf - real
     return {
         # theta r/w 8, grad 2, q_m r/w 2, q_v r/w 2 per element; absmax m/v r/w per block
@@ -38,7 +63,7 @@ def algorithmic_bytes(plan, specs, total_blocks):
         # read fp32 4 + write bf16 2 per element; zero padding 2
         "pack_shard": 6 * real + 2 * pad,
         # read bf16 2 + write bf16 2 per element
-        "unpack_full": 4 * real,
+        "unpack_full": 4 * unpack_real,
         # read bf16 over the whole selection
         "group_l2norm": 2 * buf,
         # write bf16 over the whole selection
@@ -75,14 +100,14 @@ def cpu_baseline(w, budget_s: float):
 
     L = oracle.Layout(w.specs, w.m, w.g_coll)
     theta = np.zeros(L.total, dtype=np.float32)
-    grad = np.zeros(L.total, dtype=np.uint16)
-    views = []
+    grads = [np.zeros(L.total, dtype=np.uint16) for _ in range(2)]
     for i, s in enumerate(w.specs):
-        v = synth.uniform_params(s.numel, w.seed, 2 * i).numpy()
-        views.append(v)
-        theta[L.pos[i]:L.pos[i] + s.numel] = v
-        grad[L.pos[i]:L.pos[i] + s.numel] = synth.normal_bf16(
-            s.numel, w.grad_sigma, w.seed, 2 * i + 1).view(torch.int16).numpy().view(np.uint16)
+        theta[L.pos[i]:L.pos[i] + s.numel] = synth.uniform_params(s.numel, w.seed, 2 * i).numpy()
+        for j, g in enumerate(grads):
+            g[L.pos[i]:L.pos[i] + s.numel] = synth.normal_bf16(
+                s.numel, w.grad_sigma, w.seed + 1000 * j, 2 * i + 1).view(
+                    torch.int16).numpy().view(np.uint16)
+    next_grad = np.zeros(L.total, dtype=np.uint16)
     qm = np.zeros(L.total, dtype=np.int8)
     qv = np.zeros(L.total, dtype=np.uint8)
     am = np.zeros(L.n_blocks, dtype=np.float32)
@@ -93,12 +118,13 @@ def cpu_baseline(w, budget_s: float):
     t0 = time.perf_counter()
     reps = 0
     while True:
+        grad = grads[(reps + 1) % 2]
         ss = L.group_sumsq(-1, -1, grad)
         s = oracle.clip_coef(ss, 1.0)
         L.adam8_step(-1, -1, theta, grad, qm, qv, am, av, oracle.HParams(step=reps + 1), gscale=s)
         L.pack(-1, -1, fviews, buf)
         L.unpack(-1, outs, buf)
-        L.group_zero(-1, -1, grad)
+        L.group_zero(-1, -1, next_grad)
         reps += 1
         el = time.perf_counter() - t0
         if el >= budget_s:
@@ -115,6 +141,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="llama_layer")
+    ap.add_argument("--rank", type=int, default=None,
+                    help="time one rank's ragged local shard instead of all m slices")
     ap.add_argument("--split-mode", default="cooperative", choices=["cooperative", "two_pass"])
     ap.add_argument("--chunk", type=int, default=None, help="elements per workgroup in the step")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
@@ -146,12 +174,14 @@ def main():
 
     # resident state: fp32 master, bf16 grads, int8/uint8 moments, absmax
     theta = torch.zeros(total, dtype=torch.float32, device=dev)
-    grad = torch.zeros(total, dtype=torch.int16, device=dev)
+    grads = [torch.zeros(total, dtype=torch.int16, device=dev) for _ in range(2)]
     for i, s in enumerate(w.specs):
         p = plan.pos[i]
         theta[p:p + s.numel] = synth.uniform_params(s.numel, w.seed, 2 * i, device=dev)
-        grad[p:p + s.numel] = synth.normal_bf16(s.numel, w.grad_sigma, w.seed, 2 * i + 1,
-                                                device=dev).view(torch.int16)
+        for j, g in enumerate(grads):
+            g[p:p + s.numel] = synth.normal_bf16(s.numel, w.grad_sigma, w.seed + 1000 * j,
+                                                 2 * i + 1, device=dev).view(torch.int16)
+    next_grad = torch.zeros(total, dtype=torch.int16, device=dev)
     qm = torch.zeros(total, dtype=torch.int8, device=dev)
     qv = torch.zeros(total, dtype=torch.uint8, device=dev)
     am = torch.zeros(nblk, dtype=torch.float32, device=dev)
@@ -168,29 +198,34 @@ def main():
     stream = torch.cuda.current_stream()
     sid = int(stream.cuda_stream)
     ALL = rs.RS_ALL
+    R = ALL if args.rank is None else args.rank
+    UB = ALL if args.rank is None else 0  # bucket(s) the copy-out unpacks
+    if args.rank is not None and not 0 <= args.rank < w.m:
+        raise SystemExit(f"--rank must be in 0..{w.m - 1}")
 
     ops = ["group_l2norm", "clip_coef", "adam8_step", "pack_shard", "unpack_full", "group_zero"]
 
     def step(t, ev=None):
+        grad = grads[t % 2]
         if ev is not None:
             ev[0].record(stream)
-        rs.rs_group_l2norm(plan.h, ALL, ALL, grad, rs.RS_BF16, sumsq, stream=sid)
+        rs.rs_group_l2norm(plan.h, ALL, R, grad, rs.RS_BF16, sumsq, stream=sid)
         if ev is not None:
             ev[1].record(stream)
         rs.rs_clip_coef(sumsq, 1.0, scale, stream=sid)
         if ev is not None:
             ev[2].record(stream)
-        rs.rs_adam8_step(plan.h, ALL, ALL, theta, grad, qm, qv, am, av, step=t, grad_scale=scale,
+        rs.rs_adam8_step(plan.h, ALL, R, theta, grad, qm, qv, am, av, step=t, grad_scale=scale,
                          stream=sid)
         if ev is not None:
             ev[3].record(stream)
-        rs.rs_pack_shard(plan.h, ALL, ALL, gathered, stream=sid)
+        rs.rs_pack_shard(plan.h, ALL, R, gathered, stream=sid)
         if ev is not None:
             ev[4].record(stream)
-        rs.rs_unpack_full(plan.h, ALL, gathered, stream=sid)
+        rs.rs_unpack_full(plan.h, UB, gathered, stream=sid)
         if ev is not None:
             ev[5].record(stream)
-        rs.rs_group_zero(plan.h, ALL, ALL, grad, rs.RS_BF16, stream=sid)
+        rs.rs_group_zero(plan.h, ALL, R, next_grad, rs.RS_BF16, stream=sid)
         if ev is not None:
             ev[6].record(stream)
 
@@ -219,7 +254,9 @@ def main():
         step_ms += e[0].elapsed_time(e[6])
     per_op = {o: v / args.steps for o, v in per_op.items()}
     ms_per_step = wall * 1e3 / args.steps
-    real = w.real_elems
+    real, buf, sel_blocks = selection_sizes(plan, w.specs, args.rank)
+    unpack_real = real if args.rank is None else sum(
+        s.numel for s in w.specs if int(getattr(s, "bucket", 0)) == 0)
     value = real / (ms_per_step * 1e-3)
 
     if args.pmc_calibration:
@@ -228,7 +265,7 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
 
-    ab = algorithmic_bytes(plan, w.specs, nblk)
+    ab = algorithmic_bytes(real, buf, sel_blocks, unpack_real)
     breakdown = {}
     for o in ops:
         d = {"ms": round(per_op[o], 5)}
@@ -254,11 +291,12 @@ def main():
             "workload": w.name,
             "tensors": len(w.specs),
             "real_params": real,
+            "selection": "all ranks" if args.rank is None else f"rank {args.rank}, all buckets",
             "m_ranks": w.m,
             "g_coll": w.g_coll,
             "S": plan.S[0],
             "padding": plan.padding[0],
-            "quant_blocks": nblk,
+            "quant_blocks": sel_blocks,
             "split_mode": args.split_mode,
             "chunk_elems": rs.rs_plan_chunk_elems(plan.h),
             "planner_s": round(plan_s, 4),
@@ -272,11 +310,11 @@ def main():
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(step_gbs / PEAK_GBS, 4),
-            "traffic": recorded_traffic(args.workload),
+            "traffic": recorded_traffic(args.workload) if args.rank is None else None,
         },
         "event_ms_per_step": round(step_ms / args.steps, 5),
     }
-    if args.cpu_budget > 0:
+    if args.cpu_budget > 0 and args.rank is None:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     plan.free()
     print(json.dumps(result), flush=True)
