@@ -16,7 +16,8 @@
  *     pointer argument named d_buf / d_master / d_grad / d_qm / d_qv is the
  *     base of such a full array and the library adds base_b + r*S_b itself.
  *   - Absmax arrays (one fp32 per quantisation block) are indexed by global
- *     block id: buckets in order, tensors in order, blocks in order (row
+ *     block id: buckets in order, tensors in buffer order (the given order
+ *     unless a planner order option reorders them), blocks in order (row
  *     blocks top to bottom, tiles row-major over the tile grid, elements in
  *     order).  A rank's blocks of one bucket form a contiguous id range.
  *   - bucket = RS_ALL selects every bucket, rank = RS_ALL every rank.
@@ -61,7 +62,23 @@ typedef enum {
 enum { RS_ELEMENT = 0, RS_ROWS = 1, RS_TILE = 2 };
 enum { RS_F32 = 0, RS_BF16 = 1 };
 enum { RS_VIEW_F32_SRC = 0, RS_VIEW_BF16_DST = 1 };
-enum { RS_ORDER_GIVEN = 0 };
+/* Planner options (the `order` argument of rs_plan_layout): one tensor
+ * order, optionally or-ed with RS_ALIGN_CUT_UNIT.  The planning rule of the
+ * veScale-FSDP page (section "Grouped communication") names three tensor
+ * orders: the default one, by block size and by shape; read here as the
+ * given order, block size (elements of one block) descending, and element
+ * count descending, ties keeping the given order.  RS_ALIGN_CUT_UNIT takes
+ * the other reading of the "block size" in the alignment rule: offsets are
+ * multiples of lcm(g_coll, cut unit) instead of lcm(g_coll, block
+ * elements) (only tiles narrower than their tensor, and row blocks of
+ * tensors shorter than one block, differ). */
+enum {
+    RS_ORDER_GIVEN = 0,
+    RS_ORDER_BY_BLOCK = 1,
+    RS_ORDER_BY_SIZE = 2,
+    RS_ORDER_MASK = 0xff,
+    RS_ALIGN_CUT_UNIT = 0x100
+};
 /* How a quantisation block larger than one chunk is reduced across the
  * workgroups that share it: two launches (per-chunk partial absmax, then
  * the update) or one launch in which the chunks of a block meet on
@@ -108,9 +125,12 @@ typedef struct {
  *     block),
  *   - m equal slices (Balanced Load);
  * among placements with that S_b the lexicographically smallest offsets.
- * Host only, synchronous.  order must be RS_ORDER_GIVEN.
+ * Tensors are placed in the order `order` selects (RS_ORDER_GIVEN: as
+ * given); offsets are reported per tensor in the caller's order either way.
+ * Host only, synchronous.
  * On success *out receives a new plan (free with rs_plan_free).
- * Errors: RS_EINVAL (n < 1, m < 1, g_coll < 1, bad spec, empty bucket),
+ * Errors: RS_EINVAL (n < 1, m < 1, g_coll < 1, bad spec, empty bucket,
+ * unknown order or option bits),
  * RS_EOVERFLOW (sizes beyond 2^50 elements), RS_ENOMEM. */
 rs_status rs_plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t g_coll,
                          int32_t order, rs_plan** out);

@@ -38,7 +38,7 @@ def build(force: bool = True) -> str:
 
 class _Tensor(C.Structure):
     _fields_ = [("ndim", C.c_int32), ("shape", C.c_int64 * 4), ("gran", C.c_int32),
-                ("br", C.c_int32), ("bc", C.c_int32)]
+                ("br", C.c_int32), ("bc", C.c_int32), ("align_unit", C.c_int32)]
 
 
 class _Derived(C.Structure):
@@ -110,8 +110,9 @@ def lib():
     return _lib
 
 
-def _tensor(spec) -> _Tensor:
+def _tensor(spec, align_unit: bool = False) -> _Tensor:
     t = _Tensor()
+    t.align_unit = 1 if align_unit else 0
     shp = tuple(int(s) for s in spec.shape)
     t.ndim = len(shp)
     for i, s in enumerate(shp):
@@ -122,10 +123,10 @@ def _tensor(spec) -> _Tensor:
     return t
 
 
-def _tensors(specs) -> "C.Array":
+def _tensors(specs, align_unit: bool = False) -> "C.Array":
     arr = (_Tensor * len(specs))()
     for i, s in enumerate(specs):
-        arr[i] = _tensor(s)
+        arr[i] = _tensor(s, align_unit)
     return arr
 
 
@@ -146,41 +147,69 @@ class Derived:
     nblk: int
 
 
-def derive(spec, g_coll: int) -> Derived:
+def derive(spec, g_coll: int, align_unit: bool = False) -> Derived:
     d = _Derived()
-    if lib().orc_derive(C.byref(_tensor(spec)), g_coll, C.byref(d)) != 0:
+    if lib().orc_derive(C.byref(_tensor(spec, align_unit)), g_coll, C.byref(d)) != 0:
         raise ValueError(f"invalid spec {spec}")
     return Derived(d.N, d.R, d.C, d.u, d.b, d.A, d.nblk)
 
 
-def plan_bucket(specs: Sequence, m: int, g_coll: int):
+# Tensor orders of the planning rule (veScale-FSDP page, section "Grouped
+# communication: structure-aware planning"): the default order, by block
+# size, by shape.  Read here as: given order; block size (elements of one
+# block) descending; element count descending; ties keep the given order.
+ORDER_GIVEN, ORDER_BY_BLOCK, ORDER_BY_SIZE = 0, 1, 2
+
+
+def placement_order(specs: Sequence, g_coll: int, order: int = ORDER_GIVEN) -> List[int]:
+    """Indices of specs in the order the planner places them."""
+    idx = list(range(len(specs)))
+    if order == ORDER_GIVEN:
+        return idx
+    d = [derive(s, g_coll) for s in specs]
+    if order == ORDER_BY_BLOCK:
+        return sorted(idx, key=lambda i: -d[i].b)
+    if order == ORDER_BY_SIZE:
+        return sorted(idx, key=lambda i: -d[i].N)
+    raise ValueError(f"unknown order {order}")
+
+
+def plan_bucket(specs: Sequence, m: int, g_coll: int, order: int = ORDER_GIVEN,
+                align_unit: bool = False):
     """(S, offsets) of one bucket: minimal S, lexicographically smallest
-    offsets, tensors in the given order."""
+    offsets (in placement order); offsets[i] belongs to specs[i]."""
     n = len(specs)
+    po = placement_order(specs, g_coll, order)
     off = (C.c_int64 * n)()
     S = C.c_int64()
-    rc = lib().orc_plan_bucket(_tensors(specs), n, m, g_coll, C.byref(S), off)
+    rc = lib().orc_plan_bucket(_tensors([specs[i] for i in po], align_unit), n, m, g_coll,
+                               C.byref(S), off)
     if rc != 0:
         raise ValueError("oracle planner: invalid input")
-    return int(S.value), [int(x) for x in off]
+    res = [0] * n
+    for j, i in enumerate(po):
+        res[i] = int(off[j])
+    return int(S.value), res
 
 
-def plan_bruteforce(specs: Sequence, m: int, g_coll: int, S_cap: int):
+def plan_bruteforce(specs: Sequence, m: int, g_coll: int, S_cap: int, align_unit: bool = False):
+    """Exhaustive search, tensors in the given order."""
     n = len(specs)
     off = (C.c_int64 * n)()
     S = C.c_int64()
-    rc = lib().orc_plan_bruteforce(_tensors(specs), n, m, g_coll, S_cap, C.byref(S), off)
+    rc = lib().orc_plan_bruteforce(_tensors(specs, align_unit), n, m, g_coll, S_cap, C.byref(S),
+                                   off)
     if rc != 0:
         return None
     return int(S.value), [int(x) for x in off]
 
 
-def feasible_at(specs: Sequence, m: int, g_coll: int, S: int):
+def feasible_at(specs: Sequence, m: int, g_coll: int, S: int, align_unit: bool = False):
     """Greedy placement at one fixed S, or None if infeasible."""
     n = len(specs)
     d = (_Derived * n)()
     for i, s in enumerate(specs):
-        if lib().orc_derive(C.byref(_tensor(s)), g_coll, C.byref(d[i])) != 0:
+        if lib().orc_derive(C.byref(_tensor(s, align_unit)), g_coll, C.byref(d[i])) != 0:
             raise ValueError(f"invalid spec {s}")
     off = (C.c_int64 * n)()
     if lib().orc_place_fixed_S(d, n, m, g_coll, S, off):
@@ -188,10 +217,12 @@ def feasible_at(specs: Sequence, m: int, g_coll: int, S: int):
     return None
 
 
-def check_plan(specs: Sequence, m: int, g_coll: int, S: int, offsets: Sequence[int]) -> int:
+def check_plan(specs: Sequence, m: int, g_coll: int, S: int, offsets: Sequence[int],
+               align_unit: bool = False) -> int:
+    """Invariants I1..I5; specs and offsets in placement order."""
     n = len(specs)
     off = (C.c_int64 * n)(*offsets)
-    return int(lib().orc_check_plan(_tensors(specs), n, m, g_coll, S, off))
+    return int(lib().orc_check_plan(_tensors(specs, align_unit), n, m, g_coll, S, off))
 
 
 def block_first_position(spec, p0: int, k: int) -> int:
@@ -215,10 +246,13 @@ class Layout:
     """Multi-bucket layout computed by the oracle planner: each bucket is
     planned on its own and the buckets are concatenated."""
 
-    def __init__(self, specs: Sequence, m: int, g_coll: int, bucket_plans=None):
+    def __init__(self, specs: Sequence, m: int, g_coll: int, bucket_plans=None,
+                 order: int = ORDER_GIVEN, align_unit: bool = False):
         self.specs = list(specs)
         self.m = int(m)
         self.g_coll = int(g_coll)
+        self.order = int(order)
+        self.align_unit = bool(align_unit)
         nb = 1 + max(int(s.bucket) for s in self.specs)
         self.nb = nb
         self.S: List[int] = []
@@ -231,14 +265,15 @@ class Layout:
             if not idx:
                 raise ValueError(f"bucket {b} is empty")
             key = tuple((tuple(self.specs[i].shape), self.specs[i].gran, self.specs[i].br,
-                         self.specs[i].bc) for i in idx)
+                         self.specs[i].bc) for i in idx) + (self.order, self.align_unit)
             if bucket_plans is not None:
                 S, off = bucket_plans[b]
             elif key in cache:
                 # identical tensor lists give identical plans (pure function)
                 S, off = cache[key]
             else:
-                S, off = plan_bucket([self.specs[i] for i in idx], self.m, self.g_coll)
+                S, off = plan_bucket([self.specs[i] for i in idx], self.m, self.g_coll,
+                                     self.order, self.align_unit)
                 cache[key] = (S, off)
             self.S.append(S)
             self.base.append(base)
@@ -246,10 +281,12 @@ class Layout:
                 self.offsets[i] = off[j]
             base += self.m * S
         self.total = base
-        self.derived = [derive(s, self.g_coll) for s in self.specs]
+        self.derived = [derive(s, self.g_coll, self.align_unit) for s in self.specs]
         self.pos = [self.base[int(s.bucket)] + self.offsets[i] for i, s in enumerate(self.specs)]
-        # global block ids: bucket order, then tensor order, then block order
-        order = sorted(range(len(self.specs)), key=lambda i: (int(self.specs[i].bucket), i))
+        # global block ids: bucket order, then buffer order of the tensors,
+        # then block order
+        order = sorted(range(len(self.specs)), key=lambda i: (int(self.specs[i].bucket),
+                                                              self.pos[i]))
         self.blk0 = [0] * len(self.specs)
         nblk = 0
         for i in order:

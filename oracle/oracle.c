@@ -74,7 +74,7 @@ int orc_derive(const orc_tensor* t, int64_t g_coll, orc_derived* d) {
     default:
         return -1;
     }
-    d->A = lcm64(g_coll, d->b);
+    d->A = lcm64(g_coll, t->align_unit ? d->u : d->b);
     return 0;
 }
 

@@ -42,12 +42,16 @@ extern "C" {
 enum { ORC_ELEMENT = 0, ORC_ROWS = 1, ORC_TILE = 2 };
 
 /* One RaggedShard tensor: row-major shape, granularity (ROWS: br = k rows;
- * TILE: br x bc). */
+ * TILE: br x bc).  align_unit selects the alignment reading: 0 aligns
+ * offsets to lcm(g_coll, elements of one block), 1 to lcm(g_coll, cut unit)
+ * (the alternative reading of "block size" in the planning rule of the
+ * veScale-FSDP page, section "Grouped communication"). */
 typedef struct {
     int32_t ndim;
     int64_t shape[4];
     int32_t gran;
     int32_t br, bc;
+    int32_t align_unit;
 } orc_tensor;
 
 /* Quantities derived from a tensor for a given g_coll. */
@@ -56,7 +60,7 @@ typedef struct {
     int64_t R, C;  /* 2-D view: C = last dim, R = N / C (1-D: [d0, 1]) */
     int64_t u;     /* cut unit: rank boundaries inside the tensor fall on multiples of u */
     int64_t b;     /* elements in one (clipped) non-shardable block */
-    int64_t A;     /* offset alignment lcm(g_coll, b) */
+    int64_t A;     /* offset alignment lcm(g_coll, b), or lcm(g_coll, u) with align_unit */
     int64_t nblk;  /* number of quantisation blocks */
 } orc_derived;
 

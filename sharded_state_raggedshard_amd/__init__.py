@@ -22,6 +22,10 @@ RS_ELEMENT, RS_ROWS, RS_TILE = 0, 1, 2
 RS_F32, RS_BF16 = 0, 1
 RS_VIEW_F32_SRC, RS_VIEW_BF16_DST = 0, 1
 RS_ORDER_GIVEN = 0
+RS_ORDER_BY_BLOCK = 1
+RS_ORDER_BY_SIZE = 2
+RS_ORDER_MASK = 0xff
+RS_ALIGN_CUT_UNIT = 0x100
 RS_SPLIT_TWO_PASS, RS_SPLIT_COOPERATIVE = 0, 1
 RS_ALL = -1
 
@@ -274,8 +278,8 @@ class Plan:
     """Owns one rs_plan handle and (after upload) its device workspace."""
 
     def __init__(self, specs, m: int, g_coll: int, chunk: Optional[int] = None,
-                 split_mode: int = RS_SPLIT_COOPERATIVE):
-        self.h = rs_plan_layout(specs, m, g_coll)
+                 split_mode: int = RS_SPLIT_COOPERATIVE, order: int = RS_ORDER_GIVEN):
+        self.h = rs_plan_layout(specs, m, g_coll, order)
         self.specs = list(specs)
         if chunk is not None:
             rs_plan_set_chunk(self.h, chunk)

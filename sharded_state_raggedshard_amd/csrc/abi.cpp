@@ -130,11 +130,10 @@ rs_status rs_plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int6
                          int32_t order, rs_plan** out) {
     if (!out) return fail(RS_EINVAL, "out is NULL");
     *out = nullptr;
-    if (order != RS_ORDER_GIVEN) return fail(RS_EINVAL, "only RS_ORDER_GIVEN is supported");
     try {
         rs_plan* h = new rs_plan;
         std::string err;
-        rs_status st = rs::plan_layout(specs, n, m, g_coll, h->p, err);
+        rs_status st = rs::plan_layout(specs, n, m, g_coll, order, h->p, err);
         if (st != RS_OK) {
             delete h;
             return fail(st, err);

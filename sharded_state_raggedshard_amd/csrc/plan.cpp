@@ -64,7 +64,8 @@ int64_t mod_inverse(int64_t a, int64_t n) {
     return (int64_t)t;
 }
 
-rs_status derive(const rs_tensor_spec& s, int64_t g_coll, TensorInfo& t, std::string& err) {
+rs_status derive(const rs_tensor_spec& s, int64_t g_coll, bool align_unit, TensorInfo& t,
+                 std::string& err) {
     if (s.ndim < 1 || s.ndim > 4) {
         err = "ndim must be 1..4";
         return RS_EINVAL;
@@ -132,9 +133,9 @@ rs_status derive(const rs_tensor_spec& s, int64_t g_coll, TensorInfo& t, std::st
         err = "a quantisation block holds more than 2^31 elements";
         return RS_EOVERFLOW;
     }
-    t.A = lcm_sat(g_coll, t.b);
+    t.A = lcm_sat(g_coll, align_unit ? t.u : t.b);
     if (t.A > kMaxElems) {
-        err = "alignment lcm(g_coll, block) larger than 2^50";
+        err = "offset alignment larger than 2^50";
         return RS_EOVERFLOW;
     }
     return RS_OK;
@@ -258,8 +259,8 @@ int64_t first_block_at(const Plan& p, const BucketInfo& B, int64_t P) {
 
 }  // namespace
 
-rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t g_coll, Plan& p,
-                      std::string& err) {
+rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t g_coll,
+                      int32_t options, Plan& p, std::string& err) {
     if (!specs || n < 1 || m < 1 || g_coll < 1) {
         err = "need specs != NULL, n >= 1, m >= 1, g_coll >= 1";
         return RS_EINVAL;
@@ -268,12 +269,21 @@ rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t
         err = "m or g_coll out of range";
         return RS_EINVAL;
     }
+    const int32_t order = options & RS_ORDER_MASK;
+    if (order != RS_ORDER_GIVEN && order != RS_ORDER_BY_BLOCK && order != RS_ORDER_BY_SIZE) {
+        err = "unknown tensor order";
+        return RS_EINVAL;
+    }
+    if ((options & ~(RS_ORDER_MASK | RS_ALIGN_CUT_UNIT)) != 0) {
+        err = "unknown planner option bits";
+        return RS_EINVAL;
+    }
     p.m = m;
     p.g_coll = g_coll;
     p.t.assign(n, TensorInfo{});
     int32_t nb = 0;
     for (int32_t i = 0; i < n; ++i) {
-        rs_status st = derive(specs[i], g_coll, p.t[i], err);
+        rs_status st = derive(specs[i], g_coll, (options & RS_ALIGN_CUT_UNIT) != 0, p.t[i], err);
         if (st != RS_OK) {
             err = "tensor " + std::to_string(i) + ": " + err;
             return st;
@@ -282,6 +292,15 @@ rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t
     }
     p.b.assign(nb, BucketInfo{});
     for (int32_t i = 0; i < n; ++i) p.b[p.t[i].bucket].tensors.push_back(i);
+    // placement order inside each bucket (stable: ties keep the given order)
+    for (BucketInfo& B : p.b) {
+        if (order == RS_ORDER_BY_BLOCK)
+            std::stable_sort(B.tensors.begin(), B.tensors.end(),
+                             [&](int32_t x, int32_t y) { return p.t[x].b > p.t[y].b; });
+        else if (order == RS_ORDER_BY_SIZE)
+            std::stable_sort(B.tensors.begin(), B.tensors.end(),
+                             [&](int32_t x, int32_t y) { return p.t[x].N > p.t[y].N; });
+    }
     int64_t base = 0, blk = 0;
     p.by_pos.clear();
     for (int32_t k = 0; k < nb; ++k) {

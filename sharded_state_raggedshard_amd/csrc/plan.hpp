@@ -24,7 +24,7 @@ struct TensorInfo {
 
 struct BucketInfo {
     int64_t S = 0, base = 0, real = 0, padding = 0, nblk = 0, blk0 = 0;
-    std::vector<int32_t> tensors;  // tensor indices, given order
+    std::vector<int32_t> tensors;  // tensor indices, placement order
 };
 
 struct Plan {
@@ -59,9 +59,10 @@ struct Plan {
     int64_t cb(int32_t bucket, int32_t rank) const { return chunk_begin[size_t(bucket) * (m + 1) + rank]; }
 };
 
-// Plans every bucket.  Returns RS_OK or an error with a message.
+// Plans every bucket (options: an RS_ORDER_* value, optionally with
+// RS_ALIGN_CUT_UNIT).  Returns RS_OK or an error with a message.
 rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t g_coll,
-                      Plan& out, std::string& err);
+                      int32_t options, Plan& out, std::string& err);
 
 // Builds the chunk table, rank boundaries, tensor tables and workspace
 // layout for the plan's chunk size.

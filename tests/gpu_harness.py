@@ -122,8 +122,8 @@ def assert_step_close(got: HostState, exp: HostState, mask: Optional[np.ndarray]
         assert np.allclose(a, b, rtol=1e-6, atol=0), f"{what}: {name}"
 
 
-def make_plan(specs, m, g_coll, chunk=None, mode=rs.RS_SPLIT_COOPERATIVE) -> rs.Plan:
-    return rs.Plan(specs, m, g_coll, chunk=chunk, split_mode=mode).upload()
+def make_plan(specs, m, g_coll, chunk=None, mode=rs.RS_SPLIT_COOPERATIVE, options=0) -> rs.Plan:
+    return rs.Plan(specs, m, g_coll, chunk=chunk, split_mode=mode, order=options).upload()
 
 
 def check_plan_matches(plan: rs.Plan, L: oracle.Layout):

@@ -41,8 +41,8 @@ def _oracle_rank_blocks(L, bucket):
     """rank -> (first global block id, count) from the oracle layout: a block
     belongs to the rank holding its first element."""
     ids = {}
-    for i, s in enumerate(L.specs):
-        if s.bucket != bucket:
+    for i in sorted(range(len(L.specs)), key=lambda i: L.pos[i]):  # buffer order
+        if L.specs[i].bucket != bucket:
             continue
         for k in range(L.derived[i].nblk):
             ids.setdefault(L.rank_of(L.block_first_position(i, k)), []).append(L.blk0[i] + k)
@@ -53,10 +53,10 @@ def _oracle_rank_blocks(L, bucket):
     return out
 
 
-def _compare_plan(specs, m, g):
-    h = rs.rs_plan_layout(specs, m, g)
+def _compare_plan(specs, m, g, order=0, align_unit=False):
+    h = rs.rs_plan_layout(specs, m, g, order | (rs.RS_ALIGN_CUT_UNIT if align_unit else 0))
     try:
-        L = oracle.Layout(specs, m, g)
+        L = oracle.Layout(specs, m, g, order=order, align_unit=align_unit)
         n, nb, mm, total, nblk = rs.rs_plan_info(h)
         assert (n, nb, mm, total, nblk) == (len(specs), L.nb, m, L.total, L.n_blocks)
         off, blk0 = rs.rs_plan_offsets(h)
@@ -162,7 +162,7 @@ def test_invalid_specs_and_arguments():
             2, 1)
     _expect(rs.RS_EOVERFLOW, rs.rs_plan_layout, [TensorSpec("w", (1 << 26, 1 << 26), ROWS, 2)],
             2, 16)
-    _expect(rs.RS_EINVAL, rs.rs_plan_layout, good, 2, 16, order=1)
+    _expect(rs.RS_EINVAL, rs.rs_plan_layout, good, 2, 16, order=3)
     h = rs.rs_plan_layout(good, 2, 16)
     _expect(rs.RS_EINVAL, rs.rs_plan_set_chunk, h, 100)
     _expect(rs.RS_EINVAL, rs.rs_plan_set_chunk, h, 1 << 20)
@@ -200,3 +200,57 @@ def test_replanning_is_deterministic():
     assert rs.rs_plan_chunk_count(a) == rs.rs_plan_chunk_count(b)
     rs.rs_plan_free(a)
     rs.rs_plan_free(b)
+
+
+@pytest.mark.parametrize("order", [rs.RS_ORDER_GIVEN, rs.RS_ORDER_BY_BLOCK, rs.RS_ORDER_BY_SIZE])
+@pytest.mark.parametrize("align_unit", [False, True])
+def test_planner_orders_and_alignment_reading_match_oracle(order, align_unit):
+    assert (rs.RS_ORDER_BY_BLOCK, rs.RS_ORDER_BY_SIZE) == (oracle.ORDER_BY_BLOCK,
+                                                           oracle.ORDER_BY_SIZE)
+    rng = np.random.default_rng(900 + 10 * order + int(align_unit))
+    for _ in range(200):
+        specs = synth.random_tiny_specs(rng)
+        for i, sp in enumerate(specs):
+            specs[i] = TensorSpec(sp.name, sp.shape, sp.gran, sp.br, sp.bc,
+                                  bucket=int(rng.integers(0, 2)) if i else 0)
+        # buckets must be non-empty: renumber the ones in use
+        used = sorted({sp.bucket for sp in specs})
+        specs = [TensorSpec(sp.name, sp.shape, sp.gran, sp.br, sp.bc, used.index(sp.bucket))
+                 for sp in specs]
+        m = int(rng.integers(1, 5))
+        g = int(rng.choice([1, 4, 16]))
+        h, L = _compare_plan(specs, m, g, order, align_unit)
+        for b in range(L.nb):
+            exp = _oracle_rank_blocks(L, b)
+            for r in range(m):
+                a, c = rs.rs_plan_rank_blocks(h, b, r)
+                assert (c == 0) if r not in exp else ((a, c) == exp[r])
+        rs.rs_plan_free(h)
+
+
+@pytest.mark.parametrize("name", ["tiny", "llama_layer", "llama8b_tiles", "moe"])
+@pytest.mark.parametrize("options", [rs.RS_ORDER_BY_BLOCK, rs.RS_ORDER_BY_SIZE,
+                                     rs.RS_ALIGN_CUT_UNIT])
+def test_planner_options_on_workloads(name, options):
+    w = synth.WORKLOADS[name]()
+    t0 = time.perf_counter()
+    h = rs.rs_plan_layout(w.specs, w.m, w.g_coll, options)
+    assert time.perf_counter() - t0 < 0.3
+    rs.rs_plan_free(h)
+    h, L = _compare_plan(w.specs, w.m, w.g_coll, options & rs.RS_ORDER_MASK,
+                         bool(options & rs.RS_ALIGN_CUT_UNIT))
+    for b in range(L.nb):
+        assert oracle.check_plan([L.specs[i] for i in sorted(
+            (i for i, sp in enumerate(L.specs) if sp.bucket == b), key=lambda i: L.pos[i])],
+            w.m, w.g_coll, L.S[b],
+            [L.offsets[i] for i in sorted((i for i, sp in enumerate(L.specs) if sp.bucket == b),
+                                          key=lambda i: L.pos[i])],
+            align_unit=bool(options & rs.RS_ALIGN_CUT_UNIT)) == 0
+    rs.rs_plan_free(h)
+
+
+def test_planner_rejects_unknown_options():
+    w = synth.tiny()
+    for bad in (3, 0x200, 0x1000 | 1):
+        with pytest.raises(rs.RaggedShardError):
+            rs.rs_plan_layout(w.specs, w.m, w.g_coll, bad)

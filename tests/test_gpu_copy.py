@@ -185,3 +185,31 @@ def test_l2norm_propagates_nonfinite():
     rs.rs_group_l2norm(plan.h, rs.RS_ALL, rs.RS_ALL, dev, rs.RS_F32, sumsq)
     assert math.isinf(sumsq.item())
     plan.free()
+
+
+@pytest.mark.parametrize("options", [rs.RS_ORDER_BY_SIZE, rs.RS_ORDER_BY_BLOCK | rs.RS_ALIGN_CUT_UNIT])
+@pytest.mark.parametrize("name", ["odd_g1", "multi_bucket", "tiny"])
+def test_pack_unpack_with_planner_orders(name, options):
+    """Reordered plans: the copy kernels walk the tensors in buffer order."""
+    specs, m, g = LAYOUTS[name]()
+    log(f"pack/unpack {name} options={options:#x}")
+    L = oracle.Layout(specs, m, g, order=options & rs.RS_ORDER_MASK,
+                      align_unit=bool(options & rs.RS_ALIGN_CUT_UNIT))
+    plan = make_plan(specs, m, g, options=options)
+    check_plan_matches(plan, L)
+    hv = [synth.uniform_params(s.numel, 5, i).numpy() for i, s in enumerate(specs)]
+    dv = [torch.from_numpy(v).cuda() for v in hv]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, dv)
+    buf = torch.full((L.total,), 0x1234, dtype=torch.int16, device="cuda")
+    rs.rs_pack_shard(plan.h, rs.RS_ALL, rs.RS_ALL, buf)
+    exp = np.full(L.total, 0x1234, dtype=np.uint16)
+    L.pack(-1, -1, hv, exp)
+    assert np.array_equal(dev_to_u16(buf), exp)
+    outs = [torch.zeros(s.numel, dtype=torch.int16, device="cuda") for s in specs]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_BF16_DST, outs)
+    rs.rs_unpack_full(plan.h, rs.RS_ALL, buf)
+    hexp = [np.zeros(s.numel, dtype=np.uint16) for s in specs]
+    L.unpack(-1, hexp, exp)
+    for o, e in zip(outs, hexp):
+        assert np.array_equal(dev_to_u16(o), e)
+    plan.free()

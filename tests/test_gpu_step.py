@@ -50,10 +50,11 @@ CASES = {
 }
 
 
-def _run_free(name, mode, chunk, steps=3, per_rank=False, warm=False, gscale=None):
+def _run_free(name, mode, chunk, steps=3, per_rank=False, warm=False, gscale=None, options=0):
     specs, m, g, sigma = CASES[name]()
-    L = oracle.Layout(specs, m, g)
-    plan = make_plan(specs, m, g, chunk=chunk, mode=mode)
+    L = oracle.Layout(specs, m, g, order=options & rs.RS_ORDER_MASK,
+                      align_unit=bool(options & rs.RS_ALIGN_CUT_UNIT))
+    plan = make_plan(specs, m, g, chunk=chunk, mode=mode, options=options)
     check_plan_matches(plan, L)
     hs = host_state(L, specs, seed=0, sigma=sigma, warm=warm)
     ds = DevState(hs, with_out=True)
@@ -198,3 +199,12 @@ def test_zero_grad_zero_state_is_pure_decay():
     assert np.array_equal(got.theta[real], hs.theta[real] * c)
     assert not got.qm[real].any() and not got.qv[real].any() and not got.am.any()
     plan.free()
+
+
+@pytest.mark.parametrize("options", [rs.RS_ORDER_BY_BLOCK, rs.RS_ORDER_BY_SIZE,
+                                     rs.RS_ALIGN_CUT_UNIT | rs.RS_ORDER_BY_SIZE])
+@pytest.mark.parametrize("name", ["mixed", "multi_bucket"])
+def test_step_with_planner_orders(name, options):
+    """Reordered plans: tensors sit in buffer order, block ids follow it."""
+    log(f"step {name} options={options:#x}")
+    _run_free(name, COOP, 1024, steps=2, options=options)

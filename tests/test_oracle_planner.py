@@ -174,3 +174,67 @@ def test_invariant_checker_catches_planted_mistakes():
     assert oracle.check_plan(w.specs, w.m, w.g_coll, S, bad) == 1
     # slices too small for the content
     assert oracle.check_plan(w.specs, w.m, w.g_coll, 4096, off) == 3
+
+
+# ----------------------------------------------------- planner variants
+
+def test_cut_unit_alignment_reading_tiny_hand_derivation():
+    """Other reading of the alignment rule: offsets aligned to lcm(g_coll,
+    cut unit) (golden file: S = 6144, W1 @ 0, W2 @ 6144, W3 @ 12288, bias @
+    16384)."""
+    gold = json.load(open(os.path.join(GOLDEN, "tiny_plan.json")))
+    w = synth.tiny()
+    S, off = oracle.plan_bucket(w.specs, w.m, w.g_coll, align_unit=True)
+    assert S == gold["S_if_alignment_used_cut_unit"]
+    assert off == gold["offsets_if_alignment_used_cut_unit"]
+    assert oracle.check_plan(w.specs, w.m, w.g_coll, S, off, align_unit=True) == 0
+
+
+@pytest.mark.parametrize("g_coll", [1, 4, 16])
+def test_bruteforce_agrees_with_cut_unit_alignment(g_coll):
+    rng = np.random.default_rng(3000 + g_coll)
+    for _ in range(300):
+        specs = synth.random_tiny_specs(rng)
+        m = int(rng.integers(1, 5))
+        got = oracle.plan_bucket(specs, m, g_coll, align_unit=True)
+        cap = 0
+        for s in specs:
+            d = oracle.derive(s, g_coll, align_unit=True)
+            cap += d.N + d.A
+        bf = oracle.plan_bruteforce(specs, m, g_coll, (cap + g_coll - 1) // g_coll * g_coll + g_coll,
+                                    align_unit=True)
+        assert got == bf, (specs, m, g_coll)
+
+
+@pytest.mark.parametrize("order", [oracle.ORDER_BY_BLOCK, oracle.ORDER_BY_SIZE])
+def test_orders_plan_the_permuted_list(order):
+    """A reordered plan is the brute-force optimum of the permuted list
+    (block size, or element count, descending; ties keep the given order)."""
+    rng = np.random.default_rng(4000 + order)
+    for _ in range(300):
+        specs = synth.random_tiny_specs(rng)
+        m = int(rng.integers(1, 5))
+        g = int(rng.choice([1, 2, 4, 16]))
+        d = [oracle.derive(s, g) for s in specs]
+        key = (lambda i: (-d[i].b, i)) if order == oracle.ORDER_BY_BLOCK else (lambda i: (-d[i].N, i))
+        perm = sorted(range(len(specs)), key=key)
+        S, off = oracle.plan_bucket(specs, m, g, order=order)
+        bf = oracle.plan_bruteforce([specs[i] for i in perm], m, g, _cap(specs, g))
+        assert bf is not None and S == bf[0]
+        assert [off[i] for i in perm] == bf[1]
+        assert oracle.check_plan([specs[i] for i in perm], m, g, S, [off[i] for i in perm]) == 0
+
+
+def test_order_changes_S_hand_example():
+    """m = 3, g_coll = 4; t0 = 14 elements (element blocks), t1 = [16, 1] in
+    3 x 1 tiles (cut unit 3, block 3, alignment lcm(4, 3) = 12).
+    Given order: t0 @ 0, so t1 starts at 24 at the earliest.  S = 12 leaves
+    36 elements, too few; at S = 16 the boundary 32 cuts t1 8 elements in
+    (not a multiple of 3) and t1 @ 36 overflows 48; at S = 20 t1 @ 24 ends
+    on the boundary 40.  Hence S = 20.
+    By size: t1 @ 0 is cut at 12 (a multiple of 3) when S = 12, the lower
+    bound roundup(ceil(30 / 3), 4); t0 follows @ 16.  Hence S = 12."""
+    specs = [TensorSpec("t0", (14,), ELEMENT), TensorSpec("t1", (16, 1), TILE, 3, 1)]
+    assert oracle.plan_bucket(specs, 3, 4) == (20, [0, 24])
+    assert oracle.plan_bucket(specs, 3, 4, order=oracle.ORDER_BY_SIZE) == (12, [16, 0])
+    assert oracle.plan_bucket(specs, 3, 4, order=oracle.ORDER_BY_BLOCK) == (12, [16, 0])
