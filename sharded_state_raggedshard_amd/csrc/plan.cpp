@@ -21,6 +21,7 @@
 #include "plan.hpp"
 
 #include <algorithm>
+#include <map>
 #include <limits>
 
 namespace rs {
@@ -189,9 +190,13 @@ int64_t earliest_offset(const TensorInfo& t, int32_t m, int64_t S, int64_t e) {
 
 namespace {
 
-bool place_all(const std::vector<TensorInfo*>& ts, int32_t m, int64_t S, std::vector<int64_t>& off) {
+// rest[i]: elements of tensors i.. (a lower bound on what still has to fit).
+bool place_all(const std::vector<TensorInfo*>& ts, const std::vector<int64_t>& rest, int32_t m,
+               int64_t S, std::vector<int64_t>& off) {
+    const int64_t cap = (int64_t)m * S;
     int64_t e = 0;
     for (size_t i = 0; i < ts.size(); ++i) {
+        if (e + rest[i] > cap) return false;
         int64_t o = earliest_offset(*ts[i], m, S, e);
         if (o < 0) return false;
         off[i] = o;
@@ -208,7 +213,8 @@ rs_status plan_one_bucket(std::vector<TensorInfo*>& ts, int32_t m, int64_t g, in
     // placement), so m*S >= end0; this bound also covers ceil(total / m).
     const int64_t S_lo = round_up(ceil_div(end0, m), g);
     const int64_t S_hi = round_up(end0, g);  // everything inside rank 0: always feasible
-    std::vector<int64_t> off(ts.size());
+    std::vector<int64_t> off(ts.size()), rest(ts.size() + 1, 0);
+    for (size_t i = ts.size(); i-- > 0;) rest[i] = rest[i + 1] + ts[i]->N;
     int64_t S = S_lo;
     while (S <= S_hi) {
         int64_t L = g;
@@ -226,7 +232,7 @@ rs_status plan_one_bucket(std::vector<TensorInfo*>& ts, int32_t m, int64_t g, in
             S = nxt;
             continue;
         }
-        if (place_all(ts, m, S, off)) {
+        if (place_all(ts, rest, m, S, off)) {
             for (size_t i = 0; i < ts.size(); ++i) ts[i]->off = off[i];
             S_out = S;
             return RS_OK;
@@ -303,6 +309,7 @@ rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t
     }
     int64_t base = 0, blk = 0;
     p.by_pos.clear();
+    std::map<std::vector<int64_t>, std::pair<int64_t, std::vector<int64_t>>> memo;
     for (int32_t k = 0; k < nb; ++k) {
         BucketInfo& B = p.b[k];
         if (B.tensors.empty()) {
@@ -311,8 +318,28 @@ rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t
         }
         std::vector<TensorInfo*> ts;
         for (int32_t i : B.tensors) ts.push_back(&p.t[i]);
-        rs_status st = plan_one_bucket(ts, m, g_coll, B.S, err);
-        if (st != RS_OK) return st;
+        // Buckets with the same tensor list (identical layers) get the same
+        // plan: the planner is a function of that list alone.
+        std::vector<int64_t> key;
+        key.reserve(ts.size() * 5);
+        for (const TensorInfo* t : ts) {
+            key.push_back(t->N);
+            key.push_back(t->C);
+            key.push_back(t->u);
+            key.push_back(t->b);
+            key.push_back(t->A);
+        }
+        auto hit = memo.find(key);
+        if (hit != memo.end()) {
+            B.S = hit->second.first;
+            for (size_t j = 0; j < ts.size(); ++j) ts[j]->off = hit->second.second[j];
+        } else {
+            rs_status st = plan_one_bucket(ts, m, g_coll, B.S, err);
+            if (st != RS_OK) return st;
+            std::vector<int64_t> offs(ts.size());
+            for (size_t j = 0; j < ts.size(); ++j) offs[j] = ts[j]->off;
+            memo.emplace(std::move(key), std::make_pair(B.S, std::move(offs)));
+        }
         if ((__int128)B.S * m + base > kMaxElems * 8) {
             err = "buffer larger than 2^53 elements";
             return RS_EOVERFLOW;

@@ -147,6 +147,92 @@ def llama8b_full() -> Workload:
     return Workload("llama8b_full_rows32_m1", specs, m=1, g_coll=16, grad_sigma=1e-3, steps=2)
 
 
+# ------------------------------------------------ model shape inventories
+# Tensor shapes only (architecture hyper-parameters, no weights), for the
+# planning-quality report: every matrix and vector of one layer in one
+# bucket (FSDP wraps one transformer block per bucket), the embedding in a
+# bucket of its own, the final norm and the output head in the last one.  Matrices and 1-D tensors take
+# ROWS(k) (1-D tensors as [n, 1]); fused expert tensors [E, R, C] are viewed
+# as [E * R, C].
+
+def gpt_oss_120b_shapes(rows: int) -> List[TensorSpec]:
+    """GPT-OSS-120B-shaped: 36 layers, hidden 2880, 64 query heads and 8 KV
+    heads of 64, 128 experts with fused gate/up [128, 2880, 5760] and down
+    [128, 2880, 2880] (plus biases), vocabulary 201088."""
+    h, E, ff, hd, nq, nkv, vocab, layers = 2880, 128, 2880, 64, 64, 8, 201088, 36
+    out = [TensorSpec("embed", (vocab, h), ROWS, rows, 0, 0)]
+    for l in range(layers):
+        b = l + 1
+        p = f"l{l}."
+        out += [
+            TensorSpec(p + "norm1", (h,), ROWS, rows, 0, b),
+            TensorSpec(p + "q", (nq * hd, h), ROWS, rows, 0, b),
+            TensorSpec(p + "q_bias", (nq * hd,), ROWS, rows, 0, b),
+            TensorSpec(p + "k", (nkv * hd, h), ROWS, rows, 0, b),
+            TensorSpec(p + "k_bias", (nkv * hd,), ROWS, rows, 0, b),
+            TensorSpec(p + "v", (nkv * hd, h), ROWS, rows, 0, b),
+            TensorSpec(p + "v_bias", (nkv * hd,), ROWS, rows, 0, b),
+            TensorSpec(p + "o", (h, nq * hd), ROWS, rows, 0, b),
+            TensorSpec(p + "o_bias", (h,), ROWS, rows, 0, b),
+            TensorSpec(p + "sinks", (nq,), ROWS, rows, 0, b),
+            TensorSpec(p + "norm2", (h,), ROWS, rows, 0, b),
+            TensorSpec(p + "router", (E, h), ROWS, rows, 0, b),
+            TensorSpec(p + "router_bias", (E,), ROWS, rows, 0, b),
+            TensorSpec(p + "gate_up", (E, h, 2 * ff), ROWS, rows, 0, b),
+            TensorSpec(p + "gate_up_bias", (E, 2 * ff), ROWS, rows, 0, b),
+            TensorSpec(p + "down", (E, ff, h), ROWS, rows, 0, b),
+            TensorSpec(p + "down_bias", (E, h), ROWS, rows, 0, b),
+        ]
+    out += [TensorSpec("final_norm", (h,), ROWS, rows, 0, layers + 1),
+            TensorSpec("lm_head", (vocab, h), ROWS, rows, 0, layers + 1)]
+    return out
+
+
+def deepseek_v3_shapes(rows: int) -> List[TensorSpec]:
+    """DeepSeek-V3-shaped: 61 layers, hidden 7168, multi-head latent
+    attention (128 heads, q rank 1536, kv rank 512, rope 64, nope 128, value
+    128), the first 3 layers dense (ffn 18432), the others 256 routed experts
+    and 1 shared expert of ffn 2048 stored as separate matrices, vocabulary
+    129280."""
+    h, layers, dense, E, eff, dff, vocab = 7168, 61, 3, 256, 2048, 18432, 129280
+    nh, qr, kvr, rope, nope, vd = 128, 1536, 512, 64, 128, 128
+    out = [TensorSpec("embed", (vocab, h), ROWS, rows, 0, 0)]
+    for l in range(layers):
+        b = l + 1
+        p = f"l{l}."
+        out += [
+            TensorSpec(p + "norm1", (h,), ROWS, rows, 0, b),
+            TensorSpec(p + "q_a", (qr, h), ROWS, rows, 0, b),
+            TensorSpec(p + "q_a_norm", (qr,), ROWS, rows, 0, b),
+            TensorSpec(p + "q_b", (nh * (nope + rope), qr), ROWS, rows, 0, b),
+            TensorSpec(p + "kv_a", (kvr + rope, h), ROWS, rows, 0, b),
+            TensorSpec(p + "kv_a_norm", (kvr,), ROWS, rows, 0, b),
+            TensorSpec(p + "kv_b", (nh * (nope + vd), kvr), ROWS, rows, 0, b),
+            TensorSpec(p + "o", (h, nh * vd), ROWS, rows, 0, b),
+            TensorSpec(p + "norm2", (h,), ROWS, rows, 0, b),
+        ]
+        if l < dense:
+            out += [TensorSpec(p + "gate", (dff, h), ROWS, rows, 0, b),
+                    TensorSpec(p + "up", (dff, h), ROWS, rows, 0, b),
+                    TensorSpec(p + "down", (h, dff), ROWS, rows, 0, b)]
+        else:
+            out += [TensorSpec(p + "router", (E, h), ROWS, rows, 0, b),
+                    TensorSpec(p + "router_bias", (E,), ROWS, rows, 0, b)]
+            for e in list(range(E)) + ["shared"]:
+                out += [TensorSpec(p + f"e{e}.gate", (eff, h), ROWS, rows, 0, b),
+                        TensorSpec(p + f"e{e}.up", (eff, h), ROWS, rows, 0, b),
+                        TensorSpec(p + f"e{e}.down", (h, eff), ROWS, rows, 0, b)]
+    out += [TensorSpec("final_norm", (h,), ROWS, rows, 0, layers + 1),
+            TensorSpec("lm_head", (vocab, h), ROWS, rows, 0, layers + 1)]
+    return out
+
+
+MODEL_SHAPES = {
+    "gpt_oss_120b": gpt_oss_120b_shapes,
+    "deepseek_v3": deepseek_v3_shapes,
+}
+
+
 WORKLOADS = {
     "tiny": tiny,
     "llama_layer": llama_layer_2048,
