@@ -106,6 +106,12 @@ def lib():
         L.orc_block_positions.argtypes = [C.POINTER(_Tensor), C.c_int64, C.c_int64, P64,
                                           C.c_int64]
         L.orc_block_positions.restype = C.c_int64
+        L.orc_e4m3.argtypes = [C.c_float]
+        L.orc_e4m3.restype = C.c_uint8
+        L.orc_e4m3_to_f32.argtypes = [C.c_uint8]
+        L.orc_e4m3_to_f32.restype = C.c_float
+        L.orc_pack_fp8.argtypes = [LP, C.c_int, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
+        L.orc_unpack_fp8.argtypes = [LP, C.c_int, C.c_void_p, C.c_void_p, C.c_void_p]
         _lib = L
     return _lib
 
@@ -240,6 +246,17 @@ def block_positions(spec, p0: int, k: int) -> np.ndarray:
     return out[:cnt]
 
 
+# --------------------------------------------------------------- fp8
+
+def e4m3(x: float) -> int:
+    """OCP E4M3 code of x (nearest, ties to even, saturating at +-448)."""
+    return int(lib().orc_e4m3(float(x)))
+
+
+def e4m3_to_f32(q: int) -> float:
+    return float(lib().orc_e4m3_to_f32(int(q)))
+
+
 # ------------------------------------------------------------------ layout
 
 class Layout:
@@ -336,6 +353,21 @@ class Layout:
         vs = [np.ascontiguousarray(v, dtype=np.float32) for v in views]
         arr = (C.c_void_p * len(vs))(*[v.ctypes.data for v in vs])
         lib().orc_pack(C.byref(self._L), bucket, rank, arr, _ptr(buf))
+
+    def pack_fp8(self, bucket: int, rank: int, views: Sequence[np.ndarray], buf: np.ndarray,
+                 scales: np.ndarray):
+        assert buf.dtype == np.uint8 and buf.size >= self.total
+        assert scales.dtype == np.float32 and scales.size >= self.n_blocks
+        vs = [np.ascontiguousarray(v, dtype=np.float32) for v in views]
+        arr = (C.c_void_p * len(vs))(*[v.ctypes.data for v in vs])
+        lib().orc_pack_fp8(C.byref(self._L), bucket, rank, arr, _ptr(buf), _ptr(scales))
+
+    def unpack_fp8(self, bucket: int, views: Sequence[np.ndarray], buf: np.ndarray,
+                   scales: np.ndarray):
+        for v in views:
+            assert v.dtype == np.uint16 and v.flags.c_contiguous
+        arr = (C.c_void_p * len(views))(*[v.ctypes.data for v in views])
+        lib().orc_unpack_fp8(C.byref(self._L), bucket, arr, _ptr(buf), _ptr(scales))
 
     def unpack(self, bucket: int, views: Sequence[np.ndarray], buf: np.ndarray):
         for v in views:

@@ -577,3 +577,88 @@ void orc_adam8_step(const orc_layout* L, int bucket, int rank, float* theta,
         free(o);
     }
 }
+
+/* ------------------------------------------------------------ FP8 copy-in */
+
+/* Value of an OCP E4M3 code: exponent field e (bias 7), mantissa m (3
+ * bits); e = 0 encodes m * 2^-9; 0x7f / 0xff are NaN. */
+static double e4m3_value(int code) {
+    int e = (code >> 3) & 0xf, m = code & 7;
+    double v = (e == 0) ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return (code & 0x80) ? -v : v;
+}
+
+float orc_e4m3_to_f32(uint8_t q) {
+    if ((q & 0x7f) == 0x7f) return NAN;
+    return (float)e4m3_value(q);
+}
+
+/* Nearest code by search over the 127 finite non-negative values (codes
+ * 0x00..0x7e, increasing with the code), ties to the even code. */
+uint8_t orc_e4m3(float x) {
+    uint8_t sign = signbit(x) ? 0x80 : 0x00;
+    if (isnan(x)) return (uint8_t)(sign | 0x7f);
+    double a = fabs((double)x);
+    if (a >= 448.0) return (uint8_t)(sign | 0x7e);
+    int lo = 0;
+    while (lo + 1 <= 0x7e && e4m3_value(lo + 1) <= a) ++lo; /* largest code with value <= a */
+    int best = lo;
+    if (lo < 0x7e) {
+        double dl = a - e4m3_value(lo), dh = e4m3_value(lo + 1) - a;
+        if (dh < dl || (dh == dl && ((lo + 1) & 1) == 0)) best = lo + 1;
+    }
+    return (uint8_t)(sign | best);
+}
+
+void orc_pack_fp8(const orc_layout* L, int bucket, int rank, const float* const* views,
+                  uint8_t* buf, float* scales) {
+    /* padding of the selected slices: 0 */
+    for (int k = 0; k < L->nb; ++k) {
+        if (bucket >= 0 && k != bucket) continue;
+        for (int r = 0; r < L->m; ++r) {
+            if (rank >= 0 && r != rank) continue;
+            int64_t lo = L->base[k] + (int64_t)r * L->S[k];
+            for (int64_t p = lo; p < lo + L->S[k]; ++p) buf[p] = 0;
+        }
+    }
+    for (int t = 0; t < L->n; ++t) {
+        int k = L->bucket_of[t];
+        if (bucket >= 0 && k != bucket) continue;
+        orc_derived d;
+        orc_derive(&L->spec[t], L->g_coll, &d);
+        int64_t* P = (int64_t*)malloc((size_t)d.b * sizeof(int64_t));
+        for (int64_t blk = 0; blk < d.nblk; ++blk) {
+            int64_t cnt = orc_block_positions(&L->spec[t], L->pos[t], blk, P, d.b);
+            if (!in_selection(L, bucket, rank, k, P[0])) continue;
+            float amax = 0.0f;
+            for (int64_t i = 0; i < cnt; ++i) {
+                float a = fabsf(views[t][P[i] - L->pos[t]]);
+                if (a > amax) amax = a;
+            }
+            float s = amax / 448.0f;
+            scales[L->blk0[t] + blk] = s;
+            for (int64_t i = 0; i < cnt; ++i) {
+                float x = views[t][P[i] - L->pos[t]];
+                buf[P[i]] = (s == 0.0f) ? 0 : orc_e4m3(x / s);
+            }
+        }
+        free(P);
+    }
+}
+
+void orc_unpack_fp8(const orc_layout* L, int bucket, uint16_t* const* views, const uint8_t* buf,
+                    const float* scales) {
+    for (int t = 0; t < L->n; ++t) {
+        if (bucket >= 0 && L->bucket_of[t] != bucket) continue;
+        orc_derived d;
+        orc_derive(&L->spec[t], L->g_coll, &d);
+        int64_t* P = (int64_t*)malloc((size_t)d.b * sizeof(int64_t));
+        for (int64_t blk = 0; blk < d.nblk; ++blk) {
+            int64_t cnt = orc_block_positions(&L->spec[t], L->pos[t], blk, P, d.b);
+            float s = scales[L->blk0[t] + blk];
+            for (int64_t i = 0; i < cnt; ++i)
+                views[t][P[i] - L->pos[t]] = orc_bf16(orc_e4m3_to_f32(buf[P[i]]) * s);
+        }
+        free(P);
+    }
+}

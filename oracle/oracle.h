@@ -120,6 +120,30 @@ void orc_pack(const orc_layout* L, int bucket, int rank, const float* const* vie
 /* view_t[i] = buf[pos_t + i] for every tensor of the selected buckets. */
 void orc_unpack(const orc_layout* L, int bucket, uint16_t* const* views, const uint16_t* buf);
 
+/* ---- FP8 copy-in (E4M3 with one scale per quantisation block) ----------
+ * The structure-aware case study of the veScale-FSDP page names
+ * block-wise FP8 quantisation with 128x128 blocks (section "Problem and
+ * motivation"); the scaling rule here is this library's reading: per
+ * quantisation block, s = absmax / 448 (binary32, correctly rounded),
+ * code = nearest OCP E4M3 value of x / s (correctly rounded binary32
+ * quotient), ties to the even code, saturating at +-448; absmax 0 gives
+ * s = 0 and codes 0.  The copy-out is bf16(e4m3(code) * s). */
+
+/* OCP E4M3 (bias 7, no infinities, 0x7f / 0xff NaN): nearest value of x,
+ * ties to the even code, |x| beyond 448 saturates to +-448; NaN -> 0x7f
+ * with the sign of x. */
+uint8_t orc_e4m3(float x);
+float orc_e4m3_to_f32(uint8_t q);
+
+/* buf (one byte per buffer element) and scales (one float per global block
+ * id) for the blocks of the selected slices; padding of the selected slices
+ * receives 0. */
+void orc_pack_fp8(const orc_layout* L, int bucket, int rank, const float* const* views,
+                  uint8_t* buf, float* scales);
+/* view_t[i] = bf16(e4m3(buf[pos_t + i]) * scale of its block). */
+void orc_unpack_fp8(const orc_layout* L, int bucket, uint16_t* const* views, const uint8_t* buf,
+                    const float* scales);
+
 /* Group ops over the selected slices (padding included).
  * dtype: 0 = fp32, 1 = bf16. */
 void orc_group_zero(const orc_layout* L, int bucket, int rank, void* buf, int dtype);
