@@ -211,6 +211,31 @@ rs_status rs_pack_shard(const rs_plan* plan, int32_t bucket, int32_t rank, uint1
 rs_status rs_unpack_full(const rs_plan* plan, int32_t bucket, const uint16_t* d_buf,
                          void* stream);
 
+/* ------------------------------------------------------- FP8 copy-in/out
+ * Block-wise FP8 (page section "Problem and motivation": 128 x 128 FP8
+ * blocks), made possible by RaggedShard keeping every quantisation block in
+ * one rank.  Rule (this library's reading): per quantisation block of the
+ * plan, s = absmax / 448 in binary32; code = nearest OCP E4M3 value of x / s
+ * (correctly rounded binary32 quotient), ties to the even code, saturating
+ * at +-448; absmax 0 gives s = 0 and codes 0.  One byte per buffer element
+ * (the gathered buffer is half the bf16 one), one fp32 scale per block.
+ * Non-finite inputs give undefined codes (the kernels do not fault). */
+
+/* Codes of the selected slices' blocks into d_buf (one byte per buffer
+ * element, full bucket-set array as for rs_pack_shard; padding of the
+ * selected slices set to 0) and their scales into d_scale (one float per
+ * global block id).  Reads the bound fp32 views, which must be 16-byte
+ * aligned.  Split blocks use the plan's split mode.  d_buf 16-byte aligned.
+ * Errors: RS_EINVAL, RS_ESTATE (not uploaded / views not bound). */
+rs_status rs_pack_shard_fp8(const rs_plan* plan, int32_t bucket, int32_t rank, uint8_t* d_buf,
+                            float* d_scale, void* stream);
+
+/* view_t[i] = bf16(e4m3(d_buf[pos_t + i]) * d_scale[block of the element])
+ * for every tensor of the selected bucket(s), into the bound bf16 views
+ * (16-byte aligned).  Errors as rs_unpack_full. */
+rs_status rs_unpack_full_fp8(const rs_plan* plan, int32_t bucket, const uint8_t* d_buf,
+                             const float* d_scale, void* stream);
+
 /* -------------------------------------------------------------- group ops
  * DBuffer section: one fused launch per op over all selected slices of a
  * DBuffer (padding included).  dtype RS_F32 or RS_BF16. */

@@ -106,6 +106,8 @@ def lib():
         L.orc_block_positions.argtypes = [C.POINTER(_Tensor), C.c_int64, C.c_int64, P64,
                                           C.c_int64]
         L.orc_block_positions.restype = C.c_int64
+        L.orc_fp8_block.argtypes = [C.c_int64, C.c_void_p, C.c_void_p]
+        L.orc_fp8_block.restype = C.c_float
         L.orc_e4m3.argtypes = [C.c_float]
         L.orc_e4m3.restype = C.c_uint8
         L.orc_e4m3_to_f32.argtypes = [C.c_uint8]
@@ -251,6 +253,14 @@ def block_positions(spec, p0: int, k: int) -> np.ndarray:
 def e4m3(x: float) -> int:
     """OCP E4M3 code of x (nearest, ties to even, saturating at +-448)."""
     return int(lib().orc_e4m3(float(x)))
+
+
+def fp8_block(x: np.ndarray):
+    """(scale, codes) of one quantisation block under the FP8 copy-in rule."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    q = np.zeros(x.size, dtype=np.uint8)
+    s = lib().orc_fp8_block(x.size, _ptr(x), _ptr(q))
+    return float(np.float32(s)), q
 
 
 def e4m3_to_f32(q: int) -> float:

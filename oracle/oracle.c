@@ -610,6 +610,18 @@ uint8_t orc_e4m3(float x) {
     return (uint8_t)(sign | best);
 }
 
+/* The block rule: s = absmax / 448, codes of x / s (0 when s == 0). */
+float orc_fp8_block(int64_t n, const float* x, uint8_t* codes) {
+    float amax = 0.0f;
+    for (int64_t i = 0; i < n; ++i) {
+        float a = fabsf(x[i]);
+        if (a > amax) amax = a;
+    }
+    float s = amax / 448.0f;
+    for (int64_t i = 0; i < n; ++i) codes[i] = (s == 0.0f) ? 0 : orc_e4m3(x[i] / s);
+    return s;
+}
+
 void orc_pack_fp8(const orc_layout* L, int bucket, int rank, const float* const* views,
                   uint8_t* buf, float* scales) {
     /* padding of the selected slices: 0 */
@@ -630,17 +642,13 @@ void orc_pack_fp8(const orc_layout* L, int bucket, int rank, const float* const*
         for (int64_t blk = 0; blk < d.nblk; ++blk) {
             int64_t cnt = orc_block_positions(&L->spec[t], L->pos[t], blk, P, d.b);
             if (!in_selection(L, bucket, rank, k, P[0])) continue;
-            float amax = 0.0f;
-            for (int64_t i = 0; i < cnt; ++i) {
-                float a = fabsf(views[t][P[i] - L->pos[t]]);
-                if (a > amax) amax = a;
-            }
-            float s = amax / 448.0f;
-            scales[L->blk0[t] + blk] = s;
-            for (int64_t i = 0; i < cnt; ++i) {
-                float x = views[t][P[i] - L->pos[t]];
-                buf[P[i]] = (s == 0.0f) ? 0 : orc_e4m3(x / s);
-            }
+            float* x = (float*)malloc((size_t)cnt * sizeof(float));
+            uint8_t* q = (uint8_t*)malloc((size_t)cnt);
+            for (int64_t i = 0; i < cnt; ++i) x[i] = views[t][P[i] - L->pos[t]];
+            scales[L->blk0[t] + blk] = orc_fp8_block(cnt, x, q);
+            for (int64_t i = 0; i < cnt; ++i) buf[P[i]] = q[i];
+            free(x);
+            free(q);
         }
         free(P);
     }

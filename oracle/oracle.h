@@ -135,6 +135,9 @@ void orc_unpack(const orc_layout* L, int bucket, uint16_t* const* views, const u
 uint8_t orc_e4m3(float x);
 float orc_e4m3_to_f32(uint8_t q);
 
+/* One block: returns s and writes the n codes. */
+float orc_fp8_block(int64_t n, const float* x, uint8_t* codes);
+
 /* buf (one byte per buffer element) and scales (one float per global block
  * id) for the blocks of the selected slices; padding of the selected slices
  * receives 0. */

@@ -34,6 +34,7 @@ EXPORTS = (
     "rs_plan_layout", "rs_plan_free", "rs_plan_info", "rs_plan_bucket", "rs_plan_offsets",
     "rs_plan_rank_blocks", "rs_plan_set_chunk", "rs_plan_set_split_mode", "rs_plan_chunk_count",
     "rs_plan_device_bytes", "rs_plan_upload", "rs_bind_views", "rs_pack_shard", "rs_unpack_full",
+    "rs_pack_shard_fp8", "rs_unpack_full_fp8",
     "rs_group_zero", "rs_group_scale", "rs_group_l2norm", "rs_clip_coef", "rs_adam8_step",
     "rs_plan_check_device", "rs_last_error", "rs_version",
 )
@@ -85,6 +86,8 @@ def lib() -> C.CDLL:
         "rs_bind_views": ([vp, i32, C.POINTER(vp), vp], C.c_int),
         "rs_pack_shard": ([vp, i32, i32, vp, vp], C.c_int),
         "rs_unpack_full": ([vp, i32, vp, vp], C.c_int),
+        "rs_pack_shard_fp8": ([vp, i32, i32, vp, vp, vp], C.c_int),
+        "rs_unpack_full_fp8": ([vp, i32, vp, vp, vp], C.c_int),
         "rs_group_zero": ([vp, i32, i32, vp, i32, vp], C.c_int),
         "rs_group_scale": ([vp, i32, i32, vp, i32, C.c_float, vp], C.c_int),
         "rs_group_l2norm": ([vp, i32, i32, vp, i32, vp, vp], C.c_int),
@@ -229,6 +232,15 @@ def rs_pack_shard(plan: int, bucket: int, rank: int, buf, stream=None) -> None:
 
 def rs_unpack_full(plan: int, bucket: int, buf, stream=None) -> None:
     _check(lib().rs_unpack_full(plan, bucket, _ptr(buf), _stream(stream)))
+
+
+def rs_pack_shard_fp8(plan: int, bucket: int, rank: int, buf, scale, stream=None) -> None:
+    """buf: uint8 codes (one byte per buffer element); scale: fp32 per block."""
+    _check(lib().rs_pack_shard_fp8(plan, bucket, rank, _ptr(buf), _ptr(scale), _stream(stream)))
+
+
+def rs_unpack_full_fp8(plan: int, bucket: int, buf, scale, stream=None) -> None:
+    _check(lib().rs_unpack_full_fp8(plan, bucket, _ptr(buf), _ptr(scale), _stream(stream)))
 
 
 def rs_group_zero(plan: int, bucket: int, rank: int, buf, dtype: int, stream=None) -> None:

@@ -85,6 +85,32 @@ RangeVec chunk_ranges(const rs::Plan& p, int32_t bucket, int32_t rank) {
     return v;
 }
 
+char* ws(const rs::Plan& p, size_t off);
+
+// Chunk-index ranges of the selected slices in the FP8 work table.
+RangeVec chunk_ranges8(const rs::Plan& p, int32_t bucket, int32_t rank) {
+    RangeVec v;
+    for (int32_t k = 0; k < (int32_t)p.b.size(); ++k) {
+        if (bucket != RS_ALL && k != bucket) continue;
+        if (rank == RS_ALL)
+            push_merged(v, p.cb8(k, 0), p.cb8(k, p.m));
+        else
+            push_merged(v, p.cb8(k, rank), p.cb8(k, rank + 1));
+    }
+    return v;
+}
+
+rs::Fp8Buffers fp8_buffers(const rs::Plan& p, uint8_t* buf, float* scale) {
+    rs::Fp8Buffers b;
+    b.buf = buf;
+    b.scale = scale;
+    b.chunks = reinterpret_cast<const rs::ChunkDesc*>(ws(p, p.off_chunks8));
+    b.cpart = reinterpret_cast<rs::ChunkPartial*>(ws(p, p.off_cpart8));
+    b.coop = reinterpret_cast<rs::PartSlot*>(ws(p, p.off_coop8));
+    b.counters = reinterpret_cast<rs::CoopCounters*>(ws(p, p.off_flag));
+    return b;
+}
+
 // Splits a range list into launch-sized groups.
 std::vector<rs::Ranges> groups(const RangeVec& v) {
     std::vector<rs::Ranges> out;
@@ -258,6 +284,7 @@ rs_status rs_plan_upload(rs_plan* plan, void* d_workspace, size_t bytes, void* s
         {p.off_tend, p.tend.data(), p.tend.size() * 8},
         {p.off_gidx, p.gidx.data(), p.gidx.size() * 4},
         {p.off_chunks, p.chunks.data(), p.chunks.size() * sizeof(rs::ChunkDesc)},
+        {p.off_chunks8, p.chunks8.data(), p.chunks8.size() * sizeof(rs::ChunkDesc)},
     };
     for (const Copy& c : copies) {
         if (c.bytes == 0) continue;
@@ -332,6 +359,48 @@ rs_status rs_unpack_full(const rs_plan* plan, int32_t bucket, const uint16_t* d_
     for (const rs::Ranges& r : groups(elem_ranges(p, bucket, RS_ALL))) {
         hipError_t e = rs::launch_unpack(r, tt, d_buf, as_stream(stream));
         if (e != hipSuccess) return hip_fail(e, "unpack launch");
+    }
+    return RS_OK;
+}
+
+rs_status rs_pack_shard_fp8(const rs_plan* plan, int32_t bucket, int32_t rank, uint8_t* d_buf,
+                            float* d_scale, void* stream) {
+    if (!plan || !d_buf || !d_scale) return fail(RS_EINVAL, "NULL argument");
+    const rs::Plan& p = plan->p;
+    if (!aligned(d_buf, 16) || !aligned(d_scale, 4)) return fail(RS_EINVAL, "misaligned pointer");
+    rs_status st = check_sel(p, bucket, rank);
+    if (st != RS_OK) return st;
+    if (!p.uploaded || !p.src_bound) return fail(RS_ESTATE, "plan not uploaded or fp32 views not bound");
+    if (!p.src_vec) return fail(RS_EINVAL, "FP8 copy-in needs 16-byte aligned fp32 views");
+    const rs::TensorTables tt = tables(p, true);
+    const hipStream_t s = as_stream(stream);
+    for (const rs::Ranges& r : groups(elem_ranges(p, bucket, rank))) {
+        hipError_t e = rs::launch_pad_fp8(r, tt, d_buf, s);
+        if (e != hipSuccess) return hip_fail(e, "fp8 padding launch");
+    }
+    const rs::Fp8Buffers b = fp8_buffers(p, d_buf, d_scale);
+    for (const rs::Ranges& r : groups(chunk_ranges8(p, bucket, rank))) {
+        hipError_t e = rs::launch_pack_fp8(r, b, tt, p.split_mode, p.max_nparts8, s);
+        if (e != hipSuccess) return hip_fail(e, "fp8 pack launch");
+    }
+    return RS_OK;
+}
+
+rs_status rs_unpack_full_fp8(const rs_plan* plan, int32_t bucket, const uint8_t* d_buf,
+                             const float* d_scale, void* stream) {
+    if (!plan || !d_buf || !d_scale) return fail(RS_EINVAL, "NULL argument");
+    const rs::Plan& p = plan->p;
+    if (!aligned(d_buf, 16) || !aligned(d_scale, 4)) return fail(RS_EINVAL, "misaligned pointer");
+    rs_status st = check_sel(p, bucket, RS_ALL);
+    if (st != RS_OK) return st;
+    if (!p.uploaded || !p.dst_bound) return fail(RS_ESTATE, "plan not uploaded or bf16 views not bound");
+    if (!p.dst_vec) return fail(RS_EINVAL, "FP8 copy-out needs 16-byte aligned bf16 views");
+    const rs::TensorTables tt = tables(p, false);
+    const rs::Fp8Buffers b =
+        fp8_buffers(p, const_cast<uint8_t*>(d_buf), const_cast<float*>(d_scale));
+    for (const rs::Ranges& r : groups(chunk_ranges8(p, bucket, RS_ALL))) {
+        hipError_t e = rs::launch_unpack_fp8(r, b, tt, as_stream(stream));
+        if (e != hipSuccess) return hip_fail(e, "fp8 unpack launch");
     }
     return RS_OK;
 }

@@ -46,6 +46,7 @@
 
 #include <mutex>
 
+#include "kernel_common.hpp"
 #include "launch.hpp"
 #include "raggedshard.h"
 
@@ -53,13 +54,7 @@ namespace rs {
 
 namespace {
 
-enum { MODE_PARTIAL = 0, MODE_MAIN = 1, MODE_COOP = 2 };
-
-
-// Bounded wait for the other chunks of a block (tens of ms of sleeps; a
-// normal wait is microseconds).  After any timeout every later wait of the
-// launch gives up at once, so a failed launch still ends quickly.
-constexpr uint32_t kSpinLimit = 1u << 20;
+using namespace kc;
 
 struct StepArgs {
     Ranges r;  // chunk-index ranges; wg0 = prefix counts
@@ -76,21 +71,6 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float x) {
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
-
-// Reciprocal used by the quantiser: correctly rounded 1/a, 0 for a == 0.
-__device__ __forceinline__ float quant_recip(float a) { return a == 0.0f ? 0.0f : 1.0f / a; }
-
-// Blocks whose absmax is below 2^-60 (but not 0) take the plain division.
-__device__ __forceinline__ bool quant_slow(float a) { return a < 0x1p-60f && a > 0.0f; }
-
-// m / a by Markstein's correction from y = RN(1/a); correctly rounded for
-// every quotient that can give a nonzero code when !quant_slow(a), and 0
-// for a == 0 (y = 0, m = 0).
-__device__ __forceinline__ float ratio_fast(float m, float a, float y) {
-    const float q0 = m * y;
-    const float r = __builtin_fmaf(-q0, a, m);
-    return __builtin_fmaf(r, y, q0);
-}
 
 // Correctly rounded m / a (see the file comment); a >= 0, y = quant_recip(a).
 __device__ __forceinline__ float ratio(float m, float a, float y) {
@@ -152,166 +132,7 @@ __device__ __forceinline__ float param_fast(const StepScalars& sc, float theta, 
     return (theta * sc.c_decay) - u;
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) x = fmaxf(x, __shfl_xor(x, off, 64));
-    return x;
-}
-
-// Max over the workgroup of (a, b); every thread gets the result.
-template <int NT>
-__device__ __forceinline__ void wg_max2(float& a, float& b, float* red) {
-    a = wave_max(a);
-    b = wave_max(b);
-    if (NT == 64) return;
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    if (lane == 0) {
-        red[2 * wave] = a;
-        red[2 * wave + 1] = b;
-    }
-    __syncthreads();
-    float x = 0.0f, y = 0.0f;
-#pragma unroll
-    for (int i = 0; i < NT / 64; ++i) {
-        x = fmaxf(x, red[2 * i]);
-        y = fmaxf(y, red[2 * i + 1]);
-    }
-    __syncthreads();
-    a = x;
-    b = y;
-}
-
-__device__ __forceinline__ int64_t chunk_of(const Ranges& r, int64_t wg) {
-    int i = 0;
-    while (i + 1 < r.n && r.wg0[i + 1] <= wg) ++i;
-    return r.lo[i] + (wg - r.wg0[i]);
-}
-
-// The chunks of a split block meet through per-chunk slots (PartSlot).  A
-// chunk publishes its maxima with two relaxed device-scope 64-bit stores,
-// each carrying the sequence number of this call next to the value, so a
-// reader that sees the new sequence also sees that chunk's value and no
-// ordering between the two stores or against other memory is needed.
-// Device-scope atomics bypass the per-XCD L2, so every XCD sees the same
-// words.  Wave 0 of each chunk then polls the slots of all chunks of its
-// block with relaxed loads, one chunk per lane, until all show the
-// sequence, and reduces their maxima.
-
-__device__ __forceinline__ uint32_t coop_seq(const StepBuffers& B, int64_t c) {
-    const uint64_t w = __hip_atomic_load(&B.coop[c].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    return (uint32_t)(w >> 32) + 1u;
-}
-
-__device__ __forceinline__ void coop_publish(const StepBuffers& B, int64_t c, uint32_t seq,
-                                             float am, float av) {
-    const uint64_t hi = (uint64_t)seq << 32;
-    __hip_atomic_store(&B.coop[c].m, hi | __float_as_uint(am), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-    __hip_atomic_store(&B.coop[c].v, hi | __float_as_uint(av), __ATOMIC_RELAXED,
-                       __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Run by all lanes of one wave: waits (bounded) until every chunk of the
-// block has published `seq`, and returns the block maxima in every lane.
-__device__ __forceinline__ void coop_wait(const StepBuffers& B, int64_t c0, int nparts,
-                                          uint32_t seq, float& am, float& av) {
-    const int lane = threadIdx.x & 63;
-    uint32_t spins = 0;
-    for (;;) {
-        bool ok = true;
-        float xm = 0.0f, xv = 0.0f;
-        for (int q = lane; q < nparts; q += 64) {
-            const uint64_t wm =
-                __hip_atomic_load(&B.coop[c0 + q].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint64_t wv =
-                __hip_atomic_load(&B.coop[c0 + q].v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            ok = ok && (uint32_t)(wm >> 32) == seq && (uint32_t)(wv >> 32) == seq;
-            xm = fmaxf(xm, __uint_as_float((uint32_t)wm));
-            xv = fmaxf(xv, __uint_as_float((uint32_t)wv));
-        }
-        if (__all(ok)) {
-            am = wave_max(xm);
-            av = wave_max(xv);
-            return;
-        }
-        __builtin_amdgcn_s_sleep(1);
-        ++spins;
-        bool stop = spins > kSpinLimit;
-        if (stop && lane == 0)
-            __hip_atomic_fetch_or(&B.counters->timeout, 1u, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-        if ((spins & 255u) == 0)
-            stop = stop || __hip_atomic_load(&B.counters->timeout, __ATOMIC_RELAXED,
-                                             __HIP_MEMORY_SCOPE_AGENT) != 0;
-        if (__any(stop)) {
-            am = wave_max(xm);
-            av = wave_max(xv);
-            return;
-        }
-    }
-}
-
 // ------------------------------------------------------------ vector path
-
-// Lane element offsets of a vector chunk relative to d.pos: slice k of this
-// lane starts at chunk element e = WSPAN * wave + 256 k + 4 lane, which is
-// row e / cols, column e % cols of the chunk.
-template <int KG>
-__device__ __forceinline__ void lane_offsets(const ChunkDesc& d, uint32_t (&p)[KG],
-                                             bool (&act)[KG]) {
-    constexpr int WSPAN = 256 * KG;
-    const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const int n = d.rows * d.cols;
-    // row = e / cols via a multiply-high (exact for e, cols < 2^16)
-    const uint32_t magic = d.rows > 1 ? (0xffffffffu / (uint32_t)d.cols) + 1u : 0u;
-#pragma unroll
-    for (int k = 0; k < KG; ++k) {
-        const int e = wave * WSPAN + 256 * k + 4 * lane;
-        act[k] = e < n;
-        if (d.rows == 1) {
-            p[k] = (uint32_t)e;
-        } else {
-            const uint32_t row = __umulhi((uint32_t)e, magic);
-            p[k] = row * (uint32_t)d.ld + ((uint32_t)e - row * (uint32_t)d.cols);
-        }
-    }
-}
-
-// Streaming accesses: every byte of the state is read once and written once
-// per step, so loads and stores carry the non-temporal hint.
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float4 ld_f4(const float* p) {
-    const u32x4 t = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-    return make_float4(__uint_as_float(t.x), __uint_as_float(t.y), __uint_as_float(t.z),
-                       __uint_as_float(t.w));
-}
-__device__ __forceinline__ uint2 ld_u2(const void* p) {
-    const u32x2 t = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
-    return make_uint2(t.x, t.y);
-}
-__device__ __forceinline__ uint32_t ld_u1(const void* p) {
-    return __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
-}
-__device__ __forceinline__ void st_f4(float* p, float a, float b, float c, float d) {
-    u32x4 t;
-    t.x = __float_as_uint(a);
-    t.y = __float_as_uint(b);
-    t.z = __float_as_uint(c);
-    t.w = __float_as_uint(d);
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x4*>(p));
-}
-__device__ __forceinline__ void st_u2(void* p, uint32_t a, uint32_t b) {
-    u32x2 t;
-    t.x = a;
-    t.y = b;
-    __builtin_nontemporal_store(t, reinterpret_cast<u32x2*>(p));
-}
-__device__ __forceinline__ void st_u1(void* p, uint32_t a) {
-    __builtin_nontemporal_store(a, reinterpret_cast<uint32_t*>(p));
-}
 
 // What a lane reads of one vector chunk: master, gradient and codes of its
 // 4 KG elements and the old absmax of the block(s) they belong to.
@@ -398,8 +219,14 @@ __device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const S
     const StepBuffers& B = a.b;
     const StepScalars& sc = a.sc;
     const bool split = d.nparts > 1;
-    // sequence number this call publishes (cooperative split blocks)
-    st.seq = (MODE == MODE_COOP && split) ? coop_seq(B, c) : 0u;
+    // Sequence number this call publishes (cooperative split blocks): thread
+    // 0 reads it before the workgroup max's barriers and every thread takes
+    // it from LDS after them, so no thread can read the slot after thread 0
+    // has published into it.
+    uint32_t* seq_lds = reinterpret_cast<uint32_t*>(red + 2 * (NT / 64));
+    if (MODE == MODE_COOP && split && d.run_log2 < 0 && threadIdx.x == 0)
+        *seq_lds = coop_seq(B.coop, c);
+    st.seq = 0u;
     st.wait = false;
     float lm[KG], lv[KG];
 #pragma unroll
@@ -455,8 +282,9 @@ __device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const S
                 if (threadIdx.x == 0) B.cpart[c] = ChunkPartial{x, y, in.amo[0], in.avo[0]};
                 return false;
             }
+            st.seq = *seq_lds;  // written before wg_max2's barriers
             st.wait = true;
-            if (threadIdx.x == 0) coop_publish(B, c, st.seq, x, y);
+            if (threadIdx.x == 0) coop_publish(B.coop, c, st.seq, x, y);
         }
     }
 #pragma unroll
@@ -514,7 +342,7 @@ __device__ __forceinline__ void vec_back(const ChunkDesc& d, int64_t c, const St
     uint8_t* qv_b = B.qv + d.pos;
     if (st.wait) {
         float x, y;
-        coop_wait(B, c - d.part, d.nparts, st.seq, x, y);
+        coop_wait(B.coop, B.counters, c - d.part, d.nparts, st.seq, x, y);
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             st.am[k] = x;

@@ -73,6 +73,26 @@ struct StepBuffers {
 hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const StepScalars& sc,
                         int32_t mode, int64_t chunk_elems, int32_t max_nparts, hipStream_t s);
 
+// FP8 copy-in / copy-out (chunk table of kFp8Chunk-element chunks).
+struct Fp8Buffers {
+    uint8_t* buf;          // one byte per buffer element
+    float* scale;          // one per global block id
+    const ChunkDesc* chunks;
+    ChunkPartial* cpart;   // two-pass partial absmax per chunk
+    PartSlot* coop;        // cooperative slots per chunk
+    CoopCounters* counters;
+};
+
+// Zeros the padding bytes of the selected slices (element ranges).
+hipError_t launch_pad_fp8(const Ranges& elem_ranges, const TensorTables& tt, uint8_t* buf,
+                          hipStream_t s);
+// Codes and scales of the chunks in chunk_ranges (src views in tt).
+hipError_t launch_pack_fp8(const Ranges& chunk_ranges, const Fp8Buffers& b, const TensorTables& tt,
+                           int32_t mode, int32_t max_nparts, hipStream_t s);
+// bf16 copy-out of the chunks in chunk_ranges (dst views in tt).
+hipError_t launch_unpack_fp8(const Ranges& chunk_ranges, const Fp8Buffers& b,
+                             const TensorTables& tt, hipStream_t s);
+
 // Workgroup size and 4-element groups per lane of the step kernel for a
 // chunk size.
 struct StepGeometry {

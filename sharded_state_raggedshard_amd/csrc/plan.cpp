@@ -394,7 +394,7 @@ int ilog2(int64_t x) {
 }
 
 struct ChunkBuilder {
-    Plan& p;
+    const Plan& p;
     const BucketInfo& B;
     int64_t CH;
     std::vector<ChunkDesc>& out;
@@ -526,33 +526,44 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 }  // namespace
 
-rs_status build_tables(Plan& p, std::string& err) {
+// One chunk table (chunks in buffer order, per-bucket-and-rank begin
+// indices, the most chunks of one block) for a chunk size.
+static rs_status build_chunks(const Plan& p, int64_t chunk, std::vector<ChunkDesc>& chunks,
+                              std::vector<int64_t>& begin, int32_t& max_nparts, std::string& err) {
     const int32_t nb = (int32_t)p.b.size();
     const int32_t m = p.m;
-    p.chunks.clear();
-    p.chunk_begin.assign(size_t(nb) * (m + 1), 0);
+    chunks.clear();
+    begin.assign(size_t(nb) * (m + 1), 0);
     for (int32_t k = 0; k < nb; ++k) {
         const BucketInfo& B = p.b[k];
-        size_t first = p.chunks.size();
-        ChunkBuilder cbld{p, B, p.chunk_elems, p.chunks};
+        size_t first = chunks.size();
+        ChunkBuilder cbld{p, B, chunk, chunks};
         for (int32_t i : B.tensors) cbld.tensor(p.t[i]);
         // chunks come out in buffer order, so their ranks never decrease
         size_t c = first;
         for (int32_t r = 0; r <= m; ++r) {
             int64_t lim = B.base + (int64_t)r * B.S;
-            while (c < p.chunks.size() && p.chunks[c].pos < lim) ++c;
-            p.chunk_begin[size_t(k) * (m + 1) + r] = (int64_t)c;
+            while (c < chunks.size() && chunks[c].pos < lim) ++c;
+            begin[size_t(k) * (m + 1) + r] = (int64_t)c;
         }
-        p.chunk_begin[size_t(k) * (m + 1) + m] = (int64_t)p.chunks.size();
+        begin[size_t(k) * (m + 1) + m] = (int64_t)chunks.size();
     }
-    p.max_nparts = 1;
-    for (const ChunkDesc& c : p.chunks) {
+    max_nparts = 1;
+    for (const ChunkDesc& c : chunks) {
         if (c.nparts > 65535) {
             err = "a block needs more than 65535 chunks; raise the chunk size";
             return RS_EOVERFLOW;
         }
-        p.max_nparts = std::max(p.max_nparts, c.nparts);
+        max_nparts = std::max(max_nparts, c.nparts);
     }
+    return RS_OK;
+}
+
+rs_status build_tables(Plan& p, std::string& err) {
+    rs_status st = build_chunks(p, p.chunk_elems, p.chunks, p.chunk_begin, p.max_nparts, err);
+    if (st != RS_OK) return st;
+    st = build_chunks(p, kFp8Chunk, p.chunks8, p.chunk_begin8, p.max_nparts8, err);
+    if (st != RS_OK) return st;
     // tensor tables in buffer order and the granule index
     const size_t n = p.t.size();
     p.tstart.resize(n);
@@ -589,6 +600,12 @@ rs_status build_tables(Plan& p, std::string& err) {
     off = align256(off + p.chunks.size() * sizeof(ChunkPartial));
     p.off_coop = off;
     off = align256(off + p.chunks.size() * sizeof(PartSlot));
+    p.off_chunks8 = off;
+    off = align256(off + p.chunks8.size() * sizeof(ChunkDesc));
+    p.off_cpart8 = off;
+    off = align256(off + p.chunks8.size() * sizeof(ChunkPartial));
+    p.off_coop8 = off;
+    off = align256(off + p.chunks8.size() * sizeof(PartSlot));
     p.off_l2 = off;
     off = align256(off + size_t(kL2Blocks) * 8);
     p.off_flag = off;

@@ -41,6 +41,10 @@ struct Plan {
     std::vector<ChunkDesc> chunks;
     int32_t max_nparts = 1;            // most chunks any block is split into
     std::vector<int64_t> chunk_begin;  // [nb * (m + 1)]
+    // FP8 copy-in work table (chunk size kFp8Chunk)
+    std::vector<ChunkDesc> chunks8;
+    int32_t max_nparts8 = 1;
+    std::vector<int64_t> chunk_begin8;
     std::vector<int64_t> rank_blk;     // [nb * (m + 1)] first global block id per rank
     std::vector<int32_t> gidx;         // first tensor (buffer order) ending after granule start
     std::vector<int64_t> tstart, tend; // buffer order
@@ -48,6 +52,7 @@ struct Plan {
     // workspace layout (byte offsets)
     size_t off_tstart = 0, off_tend = 0, off_src = 0, off_dst = 0, off_gidx = 0;
     size_t off_chunks = 0, off_cpart = 0, off_coop = 0, off_l2 = 0, off_flag = 0;
+    size_t off_chunks8 = 0, off_cpart8 = 0, off_coop8 = 0;
     size_t ws_bytes = 0;
 
     // device state
@@ -57,6 +62,7 @@ struct Plan {
     int32_t split_mode = RS_SPLIT_COOPERATIVE;
 
     int64_t cb(int32_t bucket, int32_t rank) const { return chunk_begin[size_t(bucket) * (m + 1) + rank]; }
+    int64_t cb8(int32_t bucket, int32_t rank) const { return chunk_begin8[size_t(bucket) * (m + 1) + rank]; }
 };
 
 // Plans every bucket (options: an RS_ORDER_* value, optionally with

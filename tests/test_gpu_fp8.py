@@ -1,0 +1,119 @@
+"""GPU parity of the FP8 copy-in (E4M3 codes + one scale per quantisation
+block) and its copy-out against the oracle: bit-exact codes, scales and
+bf16 views."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_state_raggedshard_amd as rs
+import synth
+from synth import ELEMENT, ROWS, TILE, TensorSpec
+from gpu_harness import check_plan_matches, dev_to_u16, log, make_plan
+
+pytestmark = pytest.mark.gpu
+
+
+def _kinds_specs():
+    # every chunk kind of the FP8 table (16384-element chunks): whole tiles,
+    # split row blocks (> 16384 elements), runs of small blocks, scalar
+    # blocks (odd widths), element runs, ragged edges
+    return [
+        TensorSpec("tile128", (300, 256), TILE, 128, 128),  # 128x128 tiles + clipped band
+        TensorSpec("rows_big", (40, 1040), ROWS, 32),       # 33280-element blocks: split
+        TensorSpec("tile32", (96, 64), TILE, 32, 32),
+        TensorSpec("odd", (45, 7), ROWS, 4),                # scalar
+        TensorSpec("bias", (300,), ELEMENT),
+        TensorSpec("norm", (1000,), ROWS, 32),              # runs of 32-element blocks
+        TensorSpec("tt", (300, 160), TILE, 128, 64),        # clipped columns
+    ]
+
+
+CASES = {
+    "kinds": lambda: (_kinds_specs(), 3, 16),
+    "tiny": lambda: (synth.tiny().specs, 4, 16),
+    "small_tiled_layer": lambda: (synth._llama_layer(512, 1408, 128, TILE, 128, 128, 0), 8, 16),
+}
+
+
+def _views(specs, seed):
+    hv = []
+    for i, s in enumerate(specs):
+        v = synth.uniform_params(s.numel, seed, i).numpy()
+        # a spread of magnitudes inside blocks, and an all-zero stretch
+        if s.numel > 64:
+            v[: s.numel // 7] *= np.float32(1e-3)
+            v[-16:] = 0.0
+        hv.append(v)
+    return hv
+
+
+def _check_pack(L, plan, hv, dv, bucket, rank):
+    buf = torch.full((L.total,), 0x5A, dtype=torch.uint8, device="cuda")
+    sc = torch.full((L.n_blocks,), -1.0, dtype=torch.float32, device="cuda")
+    rs.rs_pack_shard_fp8(plan.h, bucket, rank, buf, sc)
+    exp = np.full(L.total, 0x5A, dtype=np.uint8)
+    esc = np.full(L.n_blocks, -1.0, dtype=np.float32)
+    L.pack_fp8(bucket, rank, hv, exp, esc)
+    got = buf.cpu().numpy()
+    bad = np.nonzero(got != exp)[0]
+    assert bad.size == 0, f"{bad.size} codes differ, first at {bad[:5]}"
+    assert np.array_equal(sc.cpu().numpy().view(np.uint32), esc.view(np.uint32))
+    return buf, sc
+
+
+@pytest.mark.parametrize("mode", [rs.RS_SPLIT_TWO_PASS, rs.RS_SPLIT_COOPERATIVE])
+@pytest.mark.parametrize("name", list(CASES))
+def test_fp8_pack_unpack_bitexact(name, mode):
+    specs, m, g = CASES[name]()
+    log(f"fp8 {name} mode={mode}")
+    L = oracle.Layout(specs, m, g)
+    plan = make_plan(specs, m, g, mode=mode)
+    check_plan_matches(plan, L)
+    hv = _views(specs, 7)
+    dv = [torch.from_numpy(v).cuda() for v in hv]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, dv)
+    buf, sc = _check_pack(L, plan, hv, dv, rs.RS_ALL, rs.RS_ALL)
+    # per-slice calls touch only their slice and reproduce the whole
+    for r in sorted({0, m // 2, m - 1}):
+        _check_pack(L, plan, hv, dv, rs.RS_ALL, r)
+    # copy-out
+    outs = [torch.zeros(s.numel, dtype=torch.int16, device="cuda") for s in specs]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_BF16_DST, outs)
+    rs.rs_unpack_full_fp8(plan.h, rs.RS_ALL, buf, sc)
+    hexp = [np.zeros(s.numel, dtype=np.uint16) for s in specs]
+    L.unpack_fp8(-1, hexp, buf.cpu().numpy(), sc.cpu().numpy())
+    for s, o, e in zip(specs, outs, hexp):
+        assert np.array_equal(dev_to_u16(o), e), s.name
+    if mode == rs.RS_SPLIT_COOPERATIVE:
+        rs.rs_plan_check_device(plan.h)
+    plan.free()
+
+
+@pytest.mark.parametrize("w", ["llama8b_tiles_1layer", "moe"])
+def test_fp8_full_size_sampled_blocks(w):
+    """Full-size buckets: the whole bucket on the GPU, sampled blocks
+    recomputed by the oracle's block rule (blocks are independent)."""
+    wl = synth.llama8b_tiles(layers=1) if w != "moe" else synth.moe_bucket()
+    log(f"fp8 full {w}")
+    L = oracle.Layout(wl.specs, wl.m, wl.g_coll)
+    plan = make_plan(wl.specs, wl.m, wl.g_coll)
+    check_plan_matches(plan, L)
+    dv = [synth.uniform_params(s.numel, 3, i, device="cuda") for i, s in enumerate(wl.specs)]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, dv)
+    buf = torch.zeros(L.total, dtype=torch.uint8, device="cuda")
+    sc = torch.zeros(L.n_blocks, dtype=torch.float32, device="cuda")
+    rs.rs_pack_shard_fp8(plan.h, rs.RS_ALL, rs.RS_ALL, buf, sc)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for _ in range(12):
+        t = int(rng.integers(0, len(wl.specs)))
+        k = int(rng.integers(0, L.derived[t].nblk))
+        P = L.block_positions(t, k)
+        x = dv[t][torch.from_numpy(P - L.pos[t]).cuda()].cpu().numpy()
+        s, q = oracle.fp8_block(x)
+        got = buf[torch.from_numpy(P).cuda()].cpu().numpy()
+        assert np.array_equal(got, q), (t, k)
+        assert np.float32(sc[L.blk0[t] + k].item()) == np.float32(s)
+    rs.rs_plan_check_device(plan.h)
+    plan.free()
