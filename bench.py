@@ -13,6 +13,10 @@ synthetic gradient; the zeroing clears a third buffer of the same size (what
 the next backward pass would accumulate into).  Inputs are resident in HBM
 before the timed region.  Prints one JSON line.
 
+After the step, the FP8 copy-in (fp32 master -> E4M3 codes with one fp32
+scale per quantisation block) and its copy-out (codes -> bf16 views) are
+timed on their own over the same selection (`fp8_copy`; --no-fp8 skips it).
+
 With --rank R the l2norm, the step, the pack and the zeroing act on rank R's
 slices of every bucket (its ragged local shard: the per-rank work of one
 GPU in an m-GPU job), and the copy-out unpacks bucket 0 (one gathered
@@ -68,6 +72,16 @@ def algorithmic_bytes(real, buf, total_blocks, unpack_real):
         "group_l2norm": 2 * buf,
         # write bf16 over the whole selection
         "group_zero": 2 * buf,
+    }
+
+
+def fp8_algorithmic_bytes(real, buf, total_blocks, unpack_real, unpack_blocks):
+    """Bytes of the FP8 copy-in and copy-out (E4M3 code + fp32 scale per block)."""
+    return {
+        # read fp32 4 + write code 1 per element; zero padding 1; write scale 4 per block
+        "pack_shard_fp8": 5 * real + (buf - real) + 4 * total_blocks,
+        # read code 1 + write bf16 2 per element; read scale 4 per block
+        "unpack_full_fp8": 3 * unpack_real + 4 * unpack_blocks,
     }
 
 
@@ -147,6 +161,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="elements per workgroup in the step")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--no-fp8", action="store_true",
+                    help="skip the separate timing of the FP8 copy-in / copy-out")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="after the timed steps, copy a 1 GiB tensor once (a plain copy "
                          "kernel of known size for scaling HBM counters)")
@@ -259,6 +275,36 @@ def main():
         s.numel for s in w.specs if int(getattr(s, "bucket", 0)) == 0)
     value = real / (ms_per_step * 1e-3)
 
+    # FP8 copy-in (E4M3 codes + one fp32 scale per block) and its bf16 copy-out,
+    # timed on their own after the step (not part of the step above)
+    fp8 = None
+    if not args.no_fp8:
+        codes = torch.zeros(total, dtype=torch.uint8, device=dev)
+        fscale = torch.zeros(nblk, dtype=torch.float32, device=dev)
+        for _ in range(max(1, args.warmup)):
+            rs.rs_pack_shard_fp8(plan.h, ALL, R, codes, fscale, stream=sid)
+            rs.rs_unpack_full_fp8(plan.h, UB, codes, fscale, stream=sid)
+        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for e in fev:
+            e[0].record(stream)
+            rs.rs_pack_shard_fp8(plan.h, ALL, R, codes, fscale, stream=sid)
+            e[1].record(stream)
+            rs.rs_unpack_full_fp8(plan.h, UB, codes, fscale, stream=sid)
+            e[2].record(stream)
+        torch.cuda.synchronize()
+        rs.rs_plan_check_device(plan.h, stream=sid)
+        unpack_blocks = nblk if args.rank is None else sum(
+            rs.rs_plan_rank_blocks(plan.h, 0, r)[1] for r in range(w.m))
+        fab = fp8_algorithmic_bytes(real, buf, sel_blocks, unpack_real, unpack_blocks)
+        fp8 = {}
+        for j, o in enumerate(["pack_shard_fp8", "unpack_full_fp8"]):
+            ms = sum(e[j].elapsed_time(e[j + 1]) for e in fev) / args.steps
+            gbs = fab[o] / (ms * 1e-3) / 1e9
+            fp8[o] = {"ms": round(ms, 5), "alg_bytes": fab[o], "GB/s": round(gbs, 1),
+                      "frac": round(gbs / PEAK_GBS, 4)}
+        del codes, fscale
+
     if args.pmc_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
@@ -314,6 +360,8 @@ def main():
         },
         "event_ms_per_step": round(step_ms / args.steps, 5),
     }
+    if fp8 is not None:
+        result["fp8_copy"] = fp8
     if args.cpu_budget > 0 and args.rank is None:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     plan.free()
