@@ -374,10 +374,6 @@ rs_status rs_pack_shard_fp8(const rs_plan* plan, int32_t bucket, int32_t rank, u
     if (!p.src_vec) return fail(RS_EINVAL, "FP8 copy-in needs 16-byte aligned fp32 views");
     const rs::TensorTables tt = tables(p, true);
     const hipStream_t s = as_stream(stream);
-    for (const rs::Ranges& r : groups(elem_ranges(p, bucket, rank))) {
-        hipError_t e = rs::launch_pad_fp8(r, tt, d_buf, s);
-        if (e != hipSuccess) return hip_fail(e, "fp8 padding launch");
-    }
     const rs::Fp8Buffers b = fp8_buffers(p, d_buf, d_scale);
     for (const rs::Ranges& r : groups(chunk_ranges8(p, bucket, rank))) {
         hipError_t e = rs::launch_pack_fp8(r, b, tt, p.split_mode, p.max_nparts8, s);

@@ -29,7 +29,14 @@ namespace {
 
 using namespace kc;
 
-constexpr int kKG = 4;  // 4-element groups per lane
+// Lane geometry: KG 4-element groups per lane; a chunk is one pass of a
+// workgroup (NT * 4 * KG == 16384 elements).
+constexpr int kPackKG = 8;
+constexpr int kUnpackKG = 4;
+constexpr int kPackNT = int(kFp8Chunk / (4 * kPackKG));
+constexpr int kUnpackNT = int(kFp8Chunk / (4 * kUnpackKG));
+static_assert(kPackNT * 4 * kPackKG == kFp8Chunk && kUnpackNT * 4 * kUnpackKG == kFp8Chunk,
+              "an FP8 chunk is one workgroup pass");
 
 struct Fp8Args {
     Ranges r;  // chunk-index ranges of the FP8 table; wg0 = prefix counts
@@ -38,45 +45,50 @@ struct Fp8Args {
     int64_t nwg;
 };
 
-// OCP E4M3 code of a finite or infinite q: round to nearest even on the
-// E4M3 grid, |q| >= 448 saturates to 448, NaN -> 0x7f (sign kept).
-// Normal range: keep the top 3 mantissa bits with a round-to-nearest-even
-// carry (the carry may move into the exponent); below 2^-6 the grid step is
-// 2^-9, so the code is rint(|q| * 512) (0..8, where 8 is the smallest normal).
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// The E4M3 conversions are gfx950's OCP FP8 instructions: encoding rounds to
+// nearest even on the E4M3 grid (subnormals included), decoding is exact.
+// Saturation is explicit: a quotient beyond +-448 (possible only when s is
+// a subnormal binary32) is clamped first.
+__device__ __forceinline__ float e4m3_sat(float q) { return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f); }
+
+// Codes of q0..q3 in bytes 0..3.
+__device__ __forceinline__ uint32_t e4m3x4(float q0, float q1, float q2, float q3) {
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(q0), e4m3_sat(q1), 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(q2), e4m3_sat(q3), w, true);
+    return (uint32_t)w;
+}
+
 __device__ __forceinline__ uint32_t e4m3_code(float q) {
-    const uint32_t sign = (__float_as_uint(q) >> 24) & 0x80u;
-    const float a = fabsf(q);
-    uint32_t code;
-    if (!(a < 448.0f)) {
-        code = (a != a) ? 0x7fu : 0x7eu;
-    } else if (a < 0x1p-6f) {
-        code = (uint32_t)rintf(a * 512.0f);
-    } else {
-        const uint32_t b = __float_as_uint(a);
-        code = ((b + 0x7ffffu + ((b >> 20) & 1u)) >> 20) - (120u << 3);
-        if (code > 0x7eu) code = 0x7eu;
-    }
-    return sign | code;
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(q), 0.0f, 0, false) & 0xffu;
 }
 
-__device__ __forceinline__ float e4m3_value(uint32_t c) {
-    if ((c & 0x7fu) == 0x7fu) return __uint_as_float(0x7fc00000u);
-    const uint32_t e = (c >> 3) & 0xfu, m = c & 7u;
-    const float v = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-    return (c & 0x80u) ? -v : v;
+__device__ __forceinline__ float e4m3_value(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
+
+// bf16 bits of (a, b), round to nearest even, a in the low half.
+__device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+// Quotient x / s of the block rule (correctly rounded), y = RN(1 / s).  The
+// correction step of ratio_fast returns +0 for x = -0; the sign is x's.
+__device__ __forceinline__ float fp8_ratio(float x, float s, float y) {
+    return __builtin_copysignf(quant_slow(s) ? x / s : ratio_fast(x, s, y), x);
 }
 
-// Code of x in a block of scale s (s >= 0), y = RN(1 / s).
+// Code of x in a block of scale s (s >= 0; s == 0 gives code 0).
 __device__ __forceinline__ uint32_t fp8_of(float x, float s, float y) {
+    return s == 0.0f ? 0u : e4m3_code(fp8_ratio(x, s, y));
+}
+
+// Codes of four elements of one block.
+__device__ __forceinline__ uint32_t fp8x4_of(const float4& x, float s, float y) {
     if (s == 0.0f) return 0u;
-    const float q = quant_slow(s) ? x / s : ratio_fast(x, s, y);
-    return e4m3_code(q);
+    return e4m3x4(fp8_ratio(x.x, s, y), fp8_ratio(x.y, s, y), fp8_ratio(x.z, s, y),
+                  fp8_ratio(x.w, s, y));
 }
 
 // Tensor (buffer order) holding buffer position pos.
@@ -84,6 +96,17 @@ __device__ __forceinline__ int tensor_at(const TensorTables& tt, int64_t pos) {
     int j = tt.gidx[pos / kGranule];
     while (j < tt.n && tt.tend[j] <= pos) ++j;
     return j;
+}
+
+// n zero bytes from p (p is any byte address of a 16-byte aligned buffer).
+template <int NT>
+__device__ void zero_bytes(uint8_t* p, int64_t n) {
+    const int64_t head = min(n, int64_t((16 - (reinterpret_cast<uintptr_t>(p) & 15)) & 15));
+    const int64_t nv = (n - head) >> 4;
+    for (int64_t i = threadIdx.x; i < head; i += NT) p[i] = 0;
+    uint4* q = reinterpret_cast<uint4*>(p + head);
+    for (int64_t i = threadIdx.x; i < nv; i += NT) q[i] = make_uint4(0u, 0u, 0u, 0u);
+    for (int64_t i = head + 16 * nv + threadIdx.x; i < n; i += NT) p[i] = 0;
 }
 
 // Whole block of any shape, two sweeps (absmax, then codes).
@@ -118,12 +141,16 @@ __device__ void fp8_elem_chunk(const ChunkDesc& d, const float* src, uint8_t* bu
 
 template <int MODE, int NT>
 __global__ __launch_bounds__(NT) void fp8_pack_kernel(Fp8Args a) {
-    constexpr int KG = kKG, WSPAN = 256 * KG;
+    constexpr int KG = kPackKG, WSPAN = 256 * KG;
     __shared__ float red[2 * (NT / 64) + 2];
     const int64_t c = chunk_of(a.r, blockIdx.x);
     const ChunkDesc d = a.b.chunks[c];
     const bool split = d.nparts > 1;
     if (MODE == MODE_PARTIAL && (d.kind != KIND_VEC || !split)) return;
+    if (d.kind == KIND_PAD) {
+        zero_bytes<NT>(a.b.buf + d.pos, d.cols);
+        return;
+    }
     const int j = tensor_at(a.tt, d.pos);
     const float* src = reinterpret_cast<const float*>(a.tt.views[j]) + (d.pos - a.tt.tstart[j]);
     if (d.kind == KIND_SCALAR) {
@@ -149,11 +176,7 @@ __global__ __launch_bounds__(NT) void fp8_pack_kernel(Fp8Args a) {
     for (int k = 0; k < KG; ++k)
         lm[k] = fmaxf(fmaxf(fabsf(X[k].x), fabsf(X[k].y)), fmaxf(fabsf(X[k].z), fabsf(X[k].w)));
     uint8_t* out = a.b.buf + d.pos;
-    auto store = [&](int k, float s, float y) {
-        const uint32_t w = fp8_of(X[k].x, s, y) | (fp8_of(X[k].y, s, y) << 8) |
-                           (fp8_of(X[k].z, s, y) << 16) | (fp8_of(X[k].w, s, y) << 24);
-        st_u1(out + p[k], w);
-    };
+    auto store = [&](int k, float s, float y) { st_u1(out + p[k], fp8x4_of(X[k], s, y)); };
     if (d.run_log2 >= 0) {
         // runs of blocks of (1 << run_log2) elements, (1 << run_log2) / 4 lanes each
         const int lanes = (1 << d.run_log2) >> 2;
@@ -202,9 +225,10 @@ __global__ __launch_bounds__(NT) void fp8_pack_kernel(Fp8Args a) {
 // Copy-out: bf16(e4m3(code) * s) into the bound bf16 views.
 template <int NT>
 __global__ __launch_bounds__(NT) void fp8_unpack_kernel(Fp8Args a) {
-    constexpr int KG = kKG, WSPAN = 256 * KG;
+    constexpr int KG = kUnpackKG, WSPAN = 256 * KG;
     const int64_t c = chunk_of(a.r, blockIdx.x);
     const ChunkDesc d = a.b.chunks[c];
+    if (d.kind == KIND_PAD) return;
     const int j = tensor_at(a.tt, d.pos);
     uint16_t* dst = reinterpret_cast<uint16_t*>(a.tt.views[j]) + (d.pos - a.tt.tstart[j]);
     const uint8_t* in = a.b.buf + d.pos;
@@ -214,7 +238,7 @@ __global__ __launch_bounds__(NT) void fp8_unpack_kernel(Fp8Args a) {
         for (int64_t e = threadIdx.x; e < n; e += NT) {
             const int64_t r = e / d.cols, off = r * d.ld + (e - r * d.cols);
             const float s = (d.kind == KIND_ELEM) ? scale[d.blk + e] : scale[d.blk];
-            dst[off] = (uint16_t)f32_to_bf16(e4m3_value(in[off]) * s);
+            dst[off] = (uint16_t)bf16x2_bits(e4m3_value(in[off]) * s, 0.0f);
         }
         return;
     }
@@ -239,30 +263,9 @@ __global__ __launch_bounds__(NT) void fp8_unpack_kernel(Fp8Args a) {
     for (int k = 0; k < KG; ++k) {
         if (!act[k]) continue;
         const float s = S[k];
-        const uint32_t b0 = f32_to_bf16(e4m3_value(W[k] & 0xffu) * s);
-        const uint32_t b1 = f32_to_bf16(e4m3_value((W[k] >> 8) & 0xffu) * s);
-        const uint32_t b2 = f32_to_bf16(e4m3_value((W[k] >> 16) & 0xffu) * s);
-        const uint32_t b3 = f32_to_bf16(e4m3_value(W[k] >> 24) * s);
-        st_u2(dst + p[k], b0 | (b1 << 16), b2 | (b3 << 16));
-    }
-}
-
-// Zero bytes in the padding of the selected slices (copy tiles, tensor walk).
-__global__ __launch_bounds__(kCopyThreads) void fp8_pad_kernel(Ranges r, TensorTables tt,
-                                                               uint8_t* buf) {
-    int i = 0;
-    while (i + 1 < r.n && r.wg0[i + 1] <= blockIdx.x) ++i;
-    const int64_t tile = r.lo[i] / kCopyTile + (blockIdx.x - r.wg0[i]);
-    const int64_t t0 = max(r.lo[i], tile * kCopyTile), t1 = min(r.hi[i], (tile + 1) * kCopyTile);
-    int j = tt.gidx[t0 / kGranule];
-    while (j < tt.n && tt.tend[j] <= t0) ++j;
-    int64_t cur = t0;
-    while (cur < t1) {
-        const int64_t e = (j < tt.n) ? min(t1, max(cur, tt.tstart[j])) : t1;
-        for (int64_t p = cur + threadIdx.x; p < e; p += kCopyThreads) buf[p] = 0;
-        if (j >= tt.n || e >= t1) break;
-        cur = min(t1, tt.tend[j]);
-        ++j;
+        const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)W[k], false);
+        const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)W[k], true);
+        st_u2(dst + p[k], bf16x2_bits(lo.x * s, lo.y * s), bf16x2_bits(hi.x * s, hi.y * s));
     }
 }
 
@@ -302,18 +305,9 @@ Fp8Args make_args(const Ranges& chunk_ranges, const Fp8Buffers& b, const TensorT
 
 }  // namespace
 
-hipError_t launch_pad_fp8(const Ranges& elem_ranges, const TensorTables& tt, uint8_t* buf,
-                          hipStream_t s) {
-    Ranges pr = elem_ranges;
-    const int64_t ntiles = tile_ranges(pr);
-    if (ntiles == 0) return hipSuccess;
-    hipLaunchKernelGGL(fp8_pad_kernel, dim3((unsigned)ntiles), dim3(kCopyThreads), 0, s, pr, tt, buf);
-    return hipGetLastError();
-}
-
 hipError_t launch_pack_fp8(const Ranges& chunk_ranges, const Fp8Buffers& b, const TensorTables& tt,
                            int32_t mode, int32_t max_nparts, hipStream_t s) {
-    constexpr int NT = int(kFp8Chunk / 16);
+    constexpr int NT = kPackNT;
     const Fp8Args a = make_args(chunk_ranges, b, tt);
     if (a.nwg == 0) return hipSuccess;
     if (a.nwg > 0x7fffffffLL) return hipErrorInvalidValue;
@@ -335,7 +329,7 @@ hipError_t launch_pack_fp8(const Ranges& chunk_ranges, const Fp8Buffers& b, cons
 
 hipError_t launch_unpack_fp8(const Ranges& chunk_ranges, const Fp8Buffers& b,
                              const TensorTables& tt, hipStream_t s) {
-    constexpr int NT = int(kFp8Chunk / 16);
+    constexpr int NT = kUnpackNT;
     const Fp8Args a = make_args(chunk_ranges, b, tt);
     if (a.nwg == 0) return hipSuccess;
     if (a.nwg > 0x7fffffffLL) return hipErrorInvalidValue;

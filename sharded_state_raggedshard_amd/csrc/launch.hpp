@@ -83,10 +83,8 @@ struct Fp8Buffers {
     CoopCounters* counters;
 };
 
-// Zeros the padding bytes of the selected slices (element ranges).
-hipError_t launch_pad_fp8(const Ranges& elem_ranges, const TensorTables& tt, uint8_t* buf,
-                          hipStream_t s);
-// Codes and scales of the chunks in chunk_ranges (src views in tt).
+// Codes and scales of the chunks in chunk_ranges (src views in tt); padding
+// chunks are zeroed.
 hipError_t launch_pack_fp8(const Ranges& chunk_ranges, const Fp8Buffers& b, const TensorTables& tt,
                            int32_t mode, int32_t max_nparts, hipStream_t s);
 // bf16 copy-out of the chunks in chunk_ranges (dst views in tt).

@@ -527,8 +527,10 @@ size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 }  // namespace
 
 // One chunk table (chunks in buffer order, per-bucket-and-rank begin
-// indices, the most chunks of one block) for a chunk size.
-static rs_status build_chunks(const Plan& p, int64_t chunk, std::vector<ChunkDesc>& chunks,
+// indices, the most chunks of one block) for a chunk size.  With pad, the
+// padding of every slice is listed too, as KIND_PAD chunks of at most
+// `chunk` elements that never cross a rank boundary.
+static rs_status build_chunks(const Plan& p, int64_t chunk, bool pad, std::vector<ChunkDesc>& chunks,
                               std::vector<int64_t>& begin, int32_t& max_nparts, std::string& err) {
     const int32_t nb = (int32_t)p.b.size();
     const int32_t m = p.m;
@@ -538,7 +540,33 @@ static rs_status build_chunks(const Plan& p, int64_t chunk, std::vector<ChunkDes
         const BucketInfo& B = p.b[k];
         size_t first = chunks.size();
         ChunkBuilder cbld{p, B, chunk, chunks};
-        for (int32_t i : B.tensors) cbld.tensor(p.t[i]);
+        int64_t cur = B.base;  // end of what is listed so far
+        auto pad_to = [&](int64_t end) {
+            while (pad && cur < end) {
+                const int64_t rank_end = B.base + ((cur - B.base) / B.S + 1) * B.S;
+                const int64_t e = std::min({end, rank_end, cur + chunk});
+                ChunkDesc c{};
+                c.pos = cur;
+                c.blk = -1;
+                c.ld = 0;
+                c.rows = 1;
+                c.cols = (int32_t)(e - cur);
+                c.part = 0;
+                c.nparts = 1;
+                c.kind = KIND_PAD;
+                c.run_log2 = -1;
+                chunks.push_back(c);
+                cur = e;
+            }
+        };
+        // B.tensors is in buffer order
+        for (int32_t i : B.tensors) {
+            const TensorInfo& t = p.t[i];
+            pad_to(t.pos);
+            cbld.tensor(t);
+            cur = t.pos + t.N;
+        }
+        pad_to(B.base + (int64_t)m * B.S);
         // chunks come out in buffer order, so their ranks never decrease
         size_t c = first;
         for (int32_t r = 0; r <= m; ++r) {
@@ -560,9 +588,9 @@ static rs_status build_chunks(const Plan& p, int64_t chunk, std::vector<ChunkDes
 }
 
 rs_status build_tables(Plan& p, std::string& err) {
-    rs_status st = build_chunks(p, p.chunk_elems, p.chunks, p.chunk_begin, p.max_nparts, err);
+    rs_status st = build_chunks(p, p.chunk_elems, false, p.chunks, p.chunk_begin, p.max_nparts, err);
     if (st != RS_OK) return st;
-    st = build_chunks(p, kFp8Chunk, p.chunks8, p.chunk_begin8, p.max_nparts8, err);
+    st = build_chunks(p, kFp8Chunk, true, p.chunks8, p.chunk_begin8, p.max_nparts8, err);
     if (st != RS_OK) return st;
     // tensor tables in buffer order and the granule index
     const size_t n = p.t.size();

@@ -18,7 +18,9 @@ namespace rs {
 //   KIND_SCALAR one whole block of any shape/alignment (rows x cols, stride
 //               ld), element by element, two sweeps.
 //   KIND_ELEM   `cols` contiguous elements, each its own block (blk + i).
-enum ChunkKind : int32_t { KIND_VEC = 0, KIND_SCALAR = 1, KIND_ELEM = 2 };
+//   KIND_PAD    `cols` contiguous padding elements of one rank's slice (FP8
+//               table only: the copy-in zeroes them, the copy-out skips them).
+enum ChunkKind : int32_t { KIND_VEC = 0, KIND_SCALAR = 1, KIND_ELEM = 2, KIND_PAD = 3 };
 
 struct alignas(16) ChunkDesc {
     int64_t pos;   // absolute buffer element of (row 0, col 0)

@@ -57,7 +57,12 @@ def _check_pack(L, plan, hv, dv, bucket, rank):
     L.pack_fp8(bucket, rank, hv, exp, esc)
     got = buf.cpu().numpy()
     bad = np.nonzero(got != exp)[0]
-    assert bad.size == 0, f"{bad.size} codes differ, first at {bad[:5]}"
+    if bad.size:
+        x = np.zeros(L.total, dtype=np.float32)
+        for t, v in enumerate(hv):
+            x[L.pos[t]:L.pos[t] + v.size] = v
+        detail = [(int(i), float(x[i]), int(got[i]), int(exp[i])) for i in bad[:6]]
+        raise AssertionError(f"{bad.size} codes differ; (pos, x, got, expected): {detail}")
     assert np.array_equal(sc.cpu().numpy().view(np.uint32), esc.view(np.uint32))
     return buf, sc
 
@@ -87,6 +92,59 @@ def test_fp8_pack_unpack_bitexact(name, mode):
         assert np.array_equal(dev_to_u16(o), e), s.name
     if mode == rs.RS_SPLIT_COOPERATIVE:
         rs.rs_plan_check_device(plan.h)
+    plan.free()
+
+
+def _every_code_and_tie():
+    """Magnitudes <= 448 that hit every finite E4M3 value, every midpoint
+    between neighbours (ties to even) and the binary32 neighbours of each
+    midpoint, with both signs; 1024 values whose absmax is 448 (so s = 1)."""
+    pos = np.array([oracle.e4m3_to_f32(c) for c in range(127)], dtype=np.float32)
+    mids = ((pos[:-1].astype(np.float64) + pos[1:]) / 2).astype(np.float32)  # exact
+    up = np.nextafter(mids, np.float32(np.inf))
+    dn = np.nextafter(mids, np.float32(-np.inf))
+    a = np.concatenate([pos, mids, up, dn])
+    v = np.concatenate([a, -a, np.zeros(1024 - 2 * a.size, dtype=np.float32)])
+    v[-7:] = -0.0
+    assert v.size == 1024 and np.abs(v).max() == 448.0
+    return v
+
+
+def test_fp8_every_code_and_tie():
+    """The E4M3 rounding of the copy-in on every code and every tie, in the
+    three vector paths (whole contiguous blocks, 128 x 128 tiles, runs of
+    small blocks), plus a block whose scale is a binary32 subnormal (its
+    quotients can pass 448 and saturate) and an all-zero block."""
+    specs = [TensorSpec("rows", (5, 1024), ROWS, 1),
+             TensorSpec("tiles", (256, 256), TILE, 128, 128),
+             TensorSpec("small", (64, 64), ROWS, 1)]
+    m, g = 2, 16
+    log("fp8 every code and tie")
+    L = oracle.Layout(specs, m, g)
+    plan = make_plan(specs, m, g)
+    check_plan_matches(plan, L)
+    A = _every_code_and_tie()
+    rng = np.random.default_rng(11)
+    rows = np.stack([A, rng.permutation(A),
+                     np.float32(2e-38) * np.linspace(-1, 1, 1024, dtype=np.float32),
+                     # absmax / 448 = 1.4 * 2^-149 rounds to s = 2^-149: quotients up to 627
+                     np.float32(448 * 1.4 * 2.0 ** -149) * np.linspace(-1, 1, 1024, dtype=np.float32),
+                     np.where(np.arange(1024) % 2 == 0, 0.0, -0.0).astype(np.float32)])
+    tiles = np.concatenate([rng.permutation(A) for _ in range(64)]).reshape(256, 256)
+    small = rng.permutation(A).reshape(16, 64).repeat(4, axis=0)
+    small[:, 0] = 448.0  # every 64-element block holds the absmax
+    hv = [rows.reshape(-1).astype(np.float32), tiles.reshape(-1).astype(np.float32),
+          small.reshape(-1).astype(np.float32)]
+    dv = [torch.from_numpy(v).cuda() for v in hv]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, dv)
+    buf, sc = _check_pack(L, plan, hv, dv, rs.RS_ALL, rs.RS_ALL)
+    outs = [torch.zeros(s.numel, dtype=torch.int16, device="cuda") for s in specs]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_BF16_DST, outs)
+    rs.rs_unpack_full_fp8(plan.h, rs.RS_ALL, buf, sc)
+    hexp = [np.zeros(s.numel, dtype=np.uint16) for s in specs]
+    L.unpack_fp8(-1, hexp, buf.cpu().numpy(), sc.cpu().numpy())
+    for s, o, e in zip(specs, outs, hexp):
+        assert np.array_equal(dev_to_u16(o), e), s.name
     plan.free()
 
 
