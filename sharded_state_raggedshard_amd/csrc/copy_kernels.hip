@@ -16,11 +16,17 @@ namespace rs {
 
 namespace {
 
-__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
-    uint32_t u = __float_as_uint(x);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
-    return (uint16_t)((u + 0x7fffu + ((u >> 16) & 1u)) >> 16);
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 bits of (a, b), a in the low half: gfx950's packed conversion, round
+// to nearest even.
+__device__ __forceinline__ uint32_t pack2(float a, float b) {
+    const f32x2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
+
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) { return (uint16_t)pack2(x, 0.0f); }
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
@@ -30,10 +36,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 load_stream(const void* p) {
     u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
     return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-__device__ __forceinline__ uint32_t pack2(float a, float b) {
-    return (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16);
 }
 
 // Which range a workgroup belongs to (ranges are few; uniform scan).
@@ -75,7 +77,27 @@ __device__ __forceinline__ void pack_seg(uint16_t* buf, const float* src, int64_
     int64_t b1 = max(b0, e & ~int64_t(7));
     for (int64_t p = s + tid; p < b0; p += kCopyThreads) buf[p] = f32_to_bf16(src[p - tstart]);
     for (int64_t p = b1 + tid; p < e; p += kCopyThreads) buf[p] = f32_to_bf16(src[p - tstart]);
-    for (int64_t p = b0 + int64_t(tid) * 8; p < b1; p += int64_t(kCopyThreads) * 8) {
+    constexpr int64_t STEP = int64_t(kCopyThreads) * 8;
+    int64_t p0 = b0 + int64_t(tid) * 8;
+    for (; p0 + 3 * STEP < b1; p0 += 4 * STEP) {
+        uint4 x[8];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const float* sp = src + (p0 + u * STEP - tstart);
+            x[2 * u] = load_stream(sp);
+            x[2 * u + 1] = load_stream(sp + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            uint4 o;
+            o.x = pack2(__uint_as_float(x[2 * u].x), __uint_as_float(x[2 * u].y));
+            o.y = pack2(__uint_as_float(x[2 * u].z), __uint_as_float(x[2 * u].w));
+            o.z = pack2(__uint_as_float(x[2 * u + 1].x), __uint_as_float(x[2 * u + 1].y));
+            o.w = pack2(__uint_as_float(x[2 * u + 1].z), __uint_as_float(x[2 * u + 1].w));
+            *reinterpret_cast<uint4*>(buf + p0 + u * STEP) = o;
+        }
+    }
+    for (int64_t p = p0; p < b1; p += STEP) {
         const float* sp = src + (p - tstart);
         const uint4 x0 = load_stream(sp);
         const uint4 x1 = load_stream(sp + 4);
@@ -134,7 +156,16 @@ __global__ __launch_bounds__(kCopyThreads) void unpack_kernel(Ranges r, TensorTa
         int64_t b1 = max(b0, e & ~int64_t(7));
         for (int64_t p = s + tid; p < b0; p += kCopyThreads) dst[p - ts] = buf[p];
         for (int64_t p = b1 + tid; p < e; p += kCopyThreads) dst[p - ts] = buf[p];
-        for (int64_t p = b0 + int64_t(tid) * 8; p < b1; p += int64_t(kCopyThreads) * 8) {
+        constexpr int64_t STEP = int64_t(kCopyThreads) * 8;
+        int64_t p0 = b0 + int64_t(tid) * 8;
+        for (; p0 + 3 * STEP < b1; p0 += 4 * STEP) {
+            uint4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = load_stream(buf + p0 + u * STEP);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) *reinterpret_cast<uint4*>(dst + (p0 + u * STEP - ts)) = v[u];
+        }
+        for (int64_t p = p0; p < b1; p += STEP) {
             uint4 v = load_stream(buf + p);
             *reinterpret_cast<uint4*>(dst + (p - ts)) = v;
         }
