@@ -82,6 +82,9 @@ def lib():
                                           C.c_int64, P64, P64]
         L.orc_check_plan.argtypes = [C.POINTER(_Tensor), C.c_int, C.c_int, C.c_int64,
                                      C.c_int64, P64]
+        L.orc_bruteforce_feasible_at.argtypes = [C.POINTER(_Tensor), C.c_int, C.c_int,
+                                                 C.c_int64, C.c_int64, P64]
+        L.orc_wide_tensor_ok.argtypes = [C.POINTER(_Tensor), C.c_int, C.c_int64, C.c_int64]
         L.orc_bf16.argtypes = [C.c_float]
         L.orc_bf16.restype = C.c_uint16
         L.orc_bf16_to_f32.argtypes = [C.c_uint16]
@@ -223,6 +226,26 @@ def feasible_at(specs: Sequence, m: int, g_coll: int, S: int, align_unit: bool =
     if lib().orc_place_fixed_S(d, n, m, g_coll, S, off):
         return [int(x) for x in off]
     return None
+
+
+def bruteforce_feasible_at(specs: Sequence, m: int, g_coll: int, S: int,
+                           align_unit: bool = False):
+    """Exhaustive search at one fixed S (tiny inputs): the lexicographically
+    smallest offsets, or None if no placement exists at S."""
+    n = len(specs)
+    off = (C.c_int64 * n)()
+    rc = lib().orc_bruteforce_feasible_at(_tensors(specs, align_unit), n, m, g_coll, S, off)
+    if rc < 0:
+        raise ValueError("invalid input")
+    return [int(x) for x in off] if rc == 1 else None
+
+
+def wide_tensor_ok(specs: Sequence, g_coll: int, S: int, align_unit: bool = False) -> bool:
+    """The planner scan's skip rule at S (False: S is skipped)."""
+    rc = lib().orc_wide_tensor_ok(_tensors(specs, align_unit), len(specs), g_coll, S)
+    if rc < 0:
+        raise ValueError("invalid input")
+    return rc == 1
 
 
 def check_plan(specs: Sequence, m: int, g_coll: int, S: int, offsets: Sequence[int],

@@ -213,6 +213,28 @@ int orc_plan_bruteforce(const orc_tensor* ts, int n, int m, int64_t g_coll, int6
     return -1;
 }
 
+int orc_bruteforce_feasible_at(const orc_tensor* ts, int n, int m, int64_t g_coll, int64_t S,
+                               int64_t* off_out) {
+    if (n < 1 || n > 16 || m < 1 || g_coll < 1 || S < 1) return -1;
+    orc_derived d[16];
+    for (int t = 0; t < n; ++t)
+        if (orc_derive(&ts[t], g_coll, &d[t])) return -1;
+    bf_ctx c = {d, n, m, S, off_out};
+    return bf_rec(&c, 0, 0);
+}
+
+int orc_wide_tensor_ok(const orc_tensor* ts, int n, int64_t g_coll, int64_t S) {
+    if (n < 1 || g_coll < 1 || S < 1) return -1;
+    orc_derived* d = (orc_derived*)calloc((size_t)n, sizeof(orc_derived));
+    if (!d) return -1;
+    int rc = 1;
+    for (int t = 0; t < n; ++t)
+        if (orc_derive(&ts[t], g_coll, &d[t])) rc = -1;
+    if (rc == 1) rc = passes_wide_tensor_test(d, n, S);
+    free(d);
+    return rc;
+}
+
 /* ------------------------------------------------------------- invariants */
 
 int64_t orc_block_positions(const orc_tensor* t, int64_t p0, int64_t k, int64_t* out,

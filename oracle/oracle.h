@@ -83,6 +83,17 @@ int orc_plan_bucket(const orc_tensor* ts, int n, int m, int64_t g_coll, int64_t*
 int orc_plan_bruteforce(const orc_tensor* ts, int n, int m, int64_t g_coll, int64_t S_cap,
                         int64_t* S_out, int64_t* off_out);
 
+/* Exhaustive feasibility at one fixed S (tiny inputs only): 1 and the
+ * lexicographically smallest offsets if some offset tuple satisfies every
+ * constraint at S, else 0; -1 on invalid input. */
+int orc_bruteforce_feasible_at(const orc_tensor* ts, int n, int m, int64_t g_coll, int64_t S,
+                               int64_t* off_out);
+
+/* The scan's skip rule: 0 if some tensor is longer than 2S while S is not a
+ * multiple of its cut unit (such an S is infeasible), else 1; -1 on invalid
+ * input. */
+int orc_wide_tensor_ok(const orc_tensor* ts, int n, int64_t g_coll, int64_t S);
+
 /* Invariants I1..I5 of a bucket plan.  Returns 0 if all hold, otherwise the
  * number (1..5) of the first violated invariant. */
 int orc_check_plan(const orc_tensor* ts, int n, int m, int64_t g_coll, int64_t S,

@@ -19,11 +19,20 @@ namespace {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// Quiet NaN with the sign of x (the copy-in's NaN rule).
+__device__ __forceinline__ uint32_t canonical_nan(float x) {
+    return ((__float_as_uint(x) >> 16) & 0x8000u) | 0x7fc0u;
+}
+
 // bf16 bits of (a, b), a in the low half: gfx950's packed conversion, round
-// to nearest even.
+// to nearest even; a NaN becomes the quiet NaN with its sign (whatever
+// payload the conversion would keep).
 __device__ __forceinline__ uint32_t pack2(float a, float b) {
     const f32x2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    uint32_t r = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+    r = a != a ? (r & 0xffff0000u) | canonical_nan(a) : r;
+    r = b != b ? (r & 0x0000ffffu) | (canonical_nan(b) << 16) : r;
+    return r;
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float x) { return (uint16_t)pack2(x, 0.0f); }

@@ -238,3 +238,27 @@ def test_order_changes_S_hand_example():
     assert oracle.plan_bucket(specs, 3, 4) == (20, [0, 24])
     assert oracle.plan_bucket(specs, 3, 4, order=oracle.ORDER_BY_SIZE) == (12, [16, 0])
     assert oracle.plan_bucket(specs, 3, 4, order=oracle.ORDER_BY_BLOCK) == (12, [16, 0])
+
+
+@pytest.mark.parametrize("g_coll", [1, 2, 4])
+def test_scan_skip_rule_rejects_only_infeasible_S(g_coll):
+    """The oracle scan skips an S when a tensor longer than 2S would need S to
+    be a multiple of its cut unit.  Every S the rule skips must have no
+    placement at all, by exhaustive enumeration at that S."""
+    rng = np.random.default_rng(77 + g_coll)
+    skipped = 0
+    cases = []
+    for _ in range(600):
+        cases.append((synth.random_tiny_specs(rng, n_max=3, elems_max=48), int(rng.integers(2, 5))))
+    # one dominant multi-row tensor over several ranks makes the rule fire
+    for R, C, k in ((12, 2, 1), (8, 3, 2), (10, 2, 3), (9, 4, 1)):
+        cases.append(([TensorSpec("big", (R, C), ROWS, k), TensorSpec("b", (3,), ELEMENT)], 4))
+        cases.append(([TensorSpec("a", (2,), ELEMENT), TensorSpec("big", (R, C), TILE, 2, 1)], 3))
+    for specs, m in cases:
+        total = sum(s.numel for s in specs)
+        S0 = -(-(-(-total // m)) // g_coll) * g_coll
+        for S in range(S0, _cap(specs, g_coll) + 1, g_coll):
+            if not oracle.wide_tensor_ok(specs, g_coll, S):
+                skipped += 1
+                assert oracle.bruteforce_feasible_at(specs, m, g_coll, S) is None, (specs, m, S)
+    assert skipped > 50
