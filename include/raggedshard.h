@@ -80,10 +80,19 @@ enum {
     RS_ALIGN_CUT_UNIT = 0x100
 };
 /* How a quantisation block larger than one chunk is reduced across the
- * workgroups that share it: two launches (per-chunk partial absmax, then
- * the update) or one launch in which the chunks of a block meet on
- * device-scope counters. */
-enum { RS_SPLIT_TWO_PASS = 0, RS_SPLIT_COOPERATIVE = 1 };
+ * workgroups that share it (int8-AdamW step and FP8 copy-in):
+ *   RS_SPLIT_TWO_PASS:    two launches (per-chunk partial absmax, then the
+ *                         update); re-reads the inputs of split blocks.
+ *   RS_SPLIT_COOPERATIVE: one launch in which the chunks of a block meet on
+ *                         device-scope slots; workgroup w takes chunk w, and
+ *                         the waits end because gfx950 starts workgroups in
+ *                         index order on each XCD (measured behaviour, not a
+ *                         HIP promise).  The fastest mode; the default.
+ *   RS_SPLIT_ORDERED:     the same single launch, but every workgroup takes
+ *                         its chunk from a counter, so the waits end whatever
+ *                         order workgroups start in (one device-scope atomic
+ *                         per workgroup; slower). */
+enum { RS_SPLIT_TWO_PASS = 0, RS_SPLIT_COOPERATIVE = 1, RS_SPLIT_ORDERED = 2 };
 
 #define RS_ALL (-1)
 
@@ -164,10 +173,11 @@ rs_status rs_plan_rank_blocks(const rs_plan* plan, int32_t bucket, int32_t rank,
  * RS_ESTATE (uploaded). */
 rs_status rs_plan_set_chunk(rs_plan* plan, int64_t chunk_elems);
 
-/* RS_SPLIT_COOPERATIVE (default) or RS_SPLIT_TWO_PASS; may change at any
- * time between calls.  The cooperative mode falls back to two launches when
- * the device cannot hold every chunk of the largest split block twice over
- * (occupancy of the step kernel times the compute units). */
+/* RS_SPLIT_COOPERATIVE (default), RS_SPLIT_ORDERED or RS_SPLIT_TWO_PASS;
+ * may change at any time between calls.  The one-launch modes fall back to
+ * two launches when the device cannot hold twice the workgroups a block can
+ * keep waiting (twice the most chunks of any block; for the cooperative
+ * mode also twice that per XCD). */
 rs_status rs_plan_set_split_mode(rs_plan* plan, int32_t mode);
 
 /* Number of chunks of the step's work table and the chunk size in effect
@@ -284,11 +294,21 @@ rs_status rs_adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float
                         uint16_t* d_bf16_out, void* stream);
 
 /* Synchronises the stream and reports a device-side failure of the
- * cooperative step: RS_EHIP if a bounded wait for the other chunks of a
- * block gave up since the last check (the affected blocks then hold
- * unspecified codes; re-upload the plan before further cooperative calls),
- * else RS_OK.  Clears the device flag. */
+ * one-launch split modes: RS_EHIP if a bounded wait for the other chunks of
+ * a block gave up since the last check, or if the caller set the status
+ * word (rs_plan_status_offset); else RS_OK.  Clears the word.  While the
+ * word is set, every one-launch step or FP8 copy-in updates each split block
+ * whole in the workgroup of its first chunk, with no wait: results stay
+ * exact, only slower.  The launch in which a wait gives up leaves the codes
+ * (or FP8 codes and scale) of that wait's block unspecified. */
 rs_status rs_plan_check_device(rs_plan* plan, void* stream);
+
+/* Byte offset, inside the uploaded workspace, of the device status word (one
+ * uint32, nonzero after a cooperative wait gave up).  A caller may read it
+ * without synchronising, or store a nonzero value to force the wait-free
+ * whole-block path of the cooperative launches.  Errors: RS_EINVAL,
+ * RS_ESTATE (not uploaded). */
+rs_status rs_plan_status_offset(const rs_plan* plan, size_t* byte_offset);
 
 /* Thread-local message of the last non-OK status ("" if none). */
 const char* rs_last_error(void);

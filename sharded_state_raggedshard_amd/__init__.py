@@ -26,7 +26,7 @@ RS_ORDER_BY_BLOCK = 1
 RS_ORDER_BY_SIZE = 2
 RS_ORDER_MASK = 0xff
 RS_ALIGN_CUT_UNIT = 0x100
-RS_SPLIT_TWO_PASS, RS_SPLIT_COOPERATIVE = 0, 1
+RS_SPLIT_TWO_PASS, RS_SPLIT_COOPERATIVE, RS_SPLIT_ORDERED = 0, 1, 2
 RS_ALL = -1
 
 # every entry point declared in include/raggedshard.h
@@ -36,7 +36,7 @@ EXPORTS = (
     "rs_plan_device_bytes", "rs_plan_upload", "rs_bind_views", "rs_pack_shard", "rs_unpack_full",
     "rs_pack_shard_fp8", "rs_unpack_full_fp8",
     "rs_group_zero", "rs_group_scale", "rs_group_l2norm", "rs_clip_coef", "rs_adam8_step",
-    "rs_plan_check_device", "rs_last_error", "rs_version",
+    "rs_plan_check_device", "rs_plan_status_offset", "rs_last_error", "rs_version",
 )
 
 
@@ -95,6 +95,7 @@ def lib() -> C.CDLL:
         "rs_adam8_step": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, C.POINTER(rs_adam_hparams), vp,
                            vp, vp], C.c_int),
         "rs_plan_check_device": ([vp, vp], C.c_int),
+        "rs_plan_status_offset": ([vp, C.POINTER(C.c_size_t)], C.c_int),
         "rs_last_error": ([], C.c_char_p),
         "rs_version": ([], C.c_char_p),
     }
@@ -274,6 +275,12 @@ def rs_adam8_step(plan: int, bucket: int, rank: int, master, grad, qm, qv, amax_
 
 def rs_plan_check_device(plan: int, stream=None) -> None:
     _check(lib().rs_plan_check_device(plan, _stream(stream)))
+
+
+def rs_plan_status_offset(plan: int) -> int:
+    off = C.c_size_t()
+    _check(lib().rs_plan_status_offset(plan, C.byref(off)))
+    return int(off.value)
 
 
 def rs_last_error() -> str:

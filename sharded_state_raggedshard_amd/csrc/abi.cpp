@@ -235,7 +235,7 @@ rs_status rs_plan_set_chunk(rs_plan* plan, int64_t chunk_elems) {
 
 rs_status rs_plan_set_split_mode(rs_plan* plan, int32_t mode) {
     if (!plan) return fail(RS_EINVAL, "plan is NULL");
-    if (mode != RS_SPLIT_TWO_PASS && mode != RS_SPLIT_COOPERATIVE)
+    if (mode != RS_SPLIT_TWO_PASS && mode != RS_SPLIT_COOPERATIVE && mode != RS_SPLIT_ORDERED)
         return fail(RS_EINVAL, "unknown split mode");
     plan->p.split_mode = mode;
     return RS_OK;
@@ -524,8 +524,18 @@ rs_status rs_plan_check_device(rs_plan* plan, void* stream) {
                            hipMemcpyHostToDevice, s);
         if (e == hipSuccess) e = hipStreamSynchronize(s);
         if (e != hipSuccess) return hip_fail(e, "clearing device status");
-        return fail(RS_EHIP, "a cooperative block wait timed out on the device");
+        return fail(RS_EHIP, "the device status word was set: a cooperative block wait gave up "
+                             "(or the caller set it); one-launch steps and FP8 copy-ins took the "
+                             "wait-free whole-block path meanwhile");
     }
+    return RS_OK;
+}
+
+rs_status rs_plan_status_offset(const rs_plan* plan, size_t* byte_offset) {
+    if (!plan || !byte_offset) return fail(RS_EINVAL, "NULL argument");
+    const rs::Plan& p = plan->p;
+    if (!p.uploaded) return fail(RS_ESTATE, "plan not uploaded");
+    *byte_offset = p.off_flag + offsetof(rs::CoopCounters, timeout);
     return RS_OK;
 }
 

@@ -32,18 +32,12 @@
 // absmax is combined either by a first launch that writes per-chunk partials
 // (two-pass) or inside one launch (cooperative): every chunk publishes its
 // maxima into its own slot, tagged with a per-call sequence number, and every
-// wave then polls the slots of its block.  The chunks of a block are
-// consecutive workgroups, and workgroups are dispatched to the XCDs in turn
-// and in index order on each XCD.  A wait can only stall for good if some
-// workgroup w is never dispatched while every workgroup resident on its XCD
-// waits; each of those has already published and waits for a chunk at or
-// after w in its own block, so all of them have indices in (w - P, w) for a
-// block of P chunks, at most ceil(P / 8) of them per XCD.  The launch uses
-// this mode only when the device holds at least 2 P workgroups, far more
-// than 8 ceil(P / 8).  Each wait is bounded all the same and reports a
-// timeout through the device status word if it ever gives up.
+// wave then polls the slots of its block (see adam8_kernel for why the waits
+// end).  Each wait is bounded all the same and reports a timeout through the
+// device status word if it ever gives up.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kernel_common.hpp"
@@ -412,41 +406,49 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
 
 // --------------------------------------------------- generic block paths
 
-// One whole block of any shape or alignment, two sweeps.
+// One whole block, two sweeps (absmax, then update and codes), element by
+// element over its pieces ds[0 .. nd): any shape, stride or alignment.
 template <int NT>
-__device__ void scalar_chunk(const ChunkDesc& d, const StepArgs& a, float s, const float* dqm,
-                             const float* dqv, float* red) {
+__device__ void block_sweeps(const ChunkDesc* ds, int nd, int64_t blk, const StepArgs& a,
+                             float s, const float* dqm, const float* dqv, float* red) {
     const StepBuffers& B = a.b;
-    const int64_t n = int64_t(d.rows) * d.cols;
-    const float am_old = B.amax_m[d.blk], av_old = B.amax_v[d.blk];
+    const float am_old = B.amax_m[blk], av_old = B.amax_v[blk];
     float lam = 0.0f, lav = 0.0f;
-    for (int64_t e = threadIdx.x; e < n; e += NT) {
-        const int64_t r = e / d.cols;
-        const int64_t p = d.pos + r * d.ld + (e - r * d.cols);
-        const float g = __uint_as_float(uint32_t(B.grad[p]) << 16) * s;
-        const float mh = dqm[uint8_t(B.qm[p])] * am_old;
-        const float vh = dqv[B.qv[p]] * av_old;
-        const Elem el = update(a.sc, 0.0f, g, mh, vh);
-        lam = fmaxf(lam, fabsf(el.m));
-        lav = fmaxf(lav, el.v);
+    for (int q = 0; q < nd; ++q) {
+        const ChunkDesc d = ds[q];
+        const int64_t n = int64_t(d.rows) * d.cols;
+        for (int64_t e = threadIdx.x; e < n; e += NT) {
+            const int64_t r = e / d.cols;
+            const int64_t p = d.pos + r * d.ld + (e - r * d.cols);
+            const float g = __uint_as_float(uint32_t(B.grad[p]) << 16) * s;
+            const float mh = dqm[uint8_t(B.qm[p])] * am_old;
+            const float vh = dqv[B.qv[p]] * av_old;
+            const Elem el = update(a.sc, 0.0f, g, mh, vh);
+            lam = fmaxf(lam, fabsf(el.m));
+            lav = fmaxf(lav, el.v);
+        }
     }
     wg_max2<NT>(lam, lav, red);
     const float ym = quant_recip(lam), yv = quant_recip(lav);
-    for (int64_t e = threadIdx.x; e < n; e += NT) {
-        const int64_t r = e / d.cols;
-        const int64_t p = d.pos + r * d.ld + (e - r * d.cols);
-        const float g = __uint_as_float(uint32_t(B.grad[p]) << 16) * s;
-        const float mh = dqm[uint8_t(B.qm[p])] * am_old;
-        const float vh = dqv[B.qv[p]] * av_old;
-        const Elem el = update(a.sc, B.theta[p], g, mh, vh);
-        B.theta[p] = el.th;
-        if (B.out) B.out[p] = (uint16_t)f32_to_bf16(el.th);
-        B.qm[p] = (int8_t)code_m(el.m, lam, ym);
-        B.qv[p] = (uint8_t)code_v(el.v, lav, yv);
+    for (int q = 0; q < nd; ++q) {
+        const ChunkDesc d = ds[q];
+        const int64_t n = int64_t(d.rows) * d.cols;
+        for (int64_t e = threadIdx.x; e < n; e += NT) {
+            const int64_t r = e / d.cols;
+            const int64_t p = d.pos + r * d.ld + (e - r * d.cols);
+            const float g = __uint_as_float(uint32_t(B.grad[p]) << 16) * s;
+            const float mh = dqm[uint8_t(B.qm[p])] * am_old;
+            const float vh = dqv[B.qv[p]] * av_old;
+            const Elem el = update(a.sc, B.theta[p], g, mh, vh);
+            B.theta[p] = el.th;
+            if (B.out) B.out[p] = (uint16_t)f32_to_bf16(el.th);
+            B.qm[p] = (int8_t)code_m(el.m, lam, ym);
+            B.qv[p] = (uint8_t)code_v(el.v, lav, yv);
+        }
     }
     if (threadIdx.x == 0) {
-        B.amax_m[d.blk] = lam;
-        B.amax_v[d.blk] = lav;
+        B.amax_m[blk] = lam;
+        B.amax_v[blk] = lav;
     }
 }
 
@@ -495,7 +497,7 @@ __device__ __forceinline__ void one_chunk(const ChunkDesc& d, int64_t c, const S
         vec_process<MODE, NT, KG>(d, c, a, s, dqm, dqv, red, in);
     } else if (MODE != MODE_PARTIAL) {
         if (d.kind == KIND_SCALAR)
-            scalar_chunk<NT>(d, a, s, dqm, dqv, red);
+            block_sweeps<NT>(a.b.chunks + c, 1, d.blk, a, s, dqm, dqv, red);
         else
             elem_chunk<NT>(d, a, s, dqm, dqv);
     }
@@ -503,20 +505,67 @@ __device__ __forceinline__ void one_chunk(const ChunkDesc& d, int64_t c, const S
 
 // One workgroup per chunk; each lane owns 4 KG elements (KG 4-element
 // groups).  MODE_PARTIAL and MODE_MAIN are the two launches of the two-pass
-// split; MODE_COOP combines split blocks inside one launch.
+// split.  MODE_COOP and MODE_ORDERED combine split blocks inside one launch
+// (cooperative slots, see the file comment): in MODE_COOP workgroup w takes
+// chunk w; in MODE_ORDERED each workgroup takes the next chunk from a
+// counter (kept by the launch: the workgroup that takes the last chunk
+// zeroes it for the next launch), so chunks are taken in increasing order
+// whatever order the hardware starts workgroups in.  Then a waiting
+// workgroup can only lack chunks not yet taken, and those all belong to the
+// one block that straddles the counter, whose fewer than P chunks already
+// taken are all the waiting workgroups there can be (P = most chunks of a
+// block); a device that holds more than P workgroups of the kernel always
+// has room to start one more, which takes the next chunk.  MODE_COOP relies
+// instead on workgroups starting in index order on each XCD (what the
+// hardware does; see launch_nt).
+//
+// Both cooperative modes read the device status word at the start: if a
+// wait gave up in an earlier launch (or the caller set the word), a split
+// block takes no wait at all -- the workgroup of its first chunk updates the
+// whole block in two sweeps and the block's other chunks do nothing.  A
+// timeout thus costs time, not state, until rs_plan_check_device clears
+// the word.
 template <int MODE, int NT, int KG>
 __global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
+    constexpr bool kCoop = MODE == MODE_COOP || MODE == MODE_ORDERED;
     __shared__ float dqm[256], dqv[256];
     __shared__ float red[2 * (NT / 64) + 2];
-    fill_tables<NT>(dqm, dqv);
-    const int64_t c = chunk_of(a.r, blockIdx.x);
-    const ChunkDesc d = a.b.chunks[c];
+    __shared__ uint32_t status;
+    __shared__ int64_t taken;
+    if (kCoop && threadIdx.x == 0) {
+        CoopCounters* k = a.b.counters;
+        status = __hip_atomic_load(&k->timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (MODE == MODE_ORDERED) {
+            const uint32_t t = __hip_atomic_fetch_add(&k->claim[0], 1u, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+            if ((int64_t)t + 1 == a.nwg)
+                __hip_atomic_store(&k->claim[0], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            taken = t;
+        }
+    }
+    // the chunk descriptor is read before the barrier where the chunk is known
+    // (its latency overlaps the status word's and the table fill)
+    int64_t c = 0;
+    ChunkDesc d;
+    if (MODE != MODE_ORDERED) {
+        c = chunk_of(a.r, blockIdx.x);
+        d = a.b.chunks[c];
+    }
+    fill_tables<NT>(dqm, dqv);  // its barrier publishes `status` and `taken`
+    if (MODE == MODE_ORDERED) {
+        c = chunk_of(a.r, taken);
+        d = a.b.chunks[c];
+    }
     const float s = a.b.gscale ? *a.b.gscale : 1.0f;
-    one_chunk<MODE, NT, KG>(d, c, a, s, dqm, dqv, red);
+    if (kCoop && status != 0u && d.kind == KIND_VEC && d.nparts > 1 && d.run_log2 < 0) {
+        if (d.part == 0) block_sweeps<NT>(a.b.chunks + c, d.nparts, d.blk, a, s, dqm, dqv, red);
+        return;
+    }
+    one_chunk<kCoop ? MODE_COOP : MODE, NT, KG>(d, c, a, s, dqm, dqv, red);
 }
 
-// Workgroups of the cooperative kernel that the device holds at once.
-template <int NT, int KG>
+// Workgroups of a cooperative kernel the device holds at once.
+template <int MODE, int NT, int KG>
 int coop_capacity() {
     static std::mutex mu;
     static int cached[64] = {0};
@@ -526,7 +575,7 @@ int coop_capacity() {
     if (cached[dev] == 0) {
         int per_cu = 0, ncu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(adam8_kernel<MODE_COOP, NT, KG>), NT, 0) !=
+                &per_cu, reinterpret_cast<const void*>(adam8_kernel<MODE, NT, KG>), NT, 0) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -538,10 +587,14 @@ int coop_capacity() {
 template <int NT, int KG>
 hipError_t launch_nt(const StepArgs& a, int32_t mode, int32_t max_nparts, hipStream_t s) {
     const dim3 grid((unsigned)a.nwg), block(NT);
-    // cooperative only with a 2x margin on residency (other work may share the device)
-    if (mode == RS_SPLIT_COOPERATIVE && max_nparts > 1 &&
-        2 * (int64_t)max_nparts <= coop_capacity<NT, KG>()) {
+    if (max_nparts > 1 && mode == RS_SPLIT_COOPERATIVE &&
+        coop_ok(max_nparts, coop_capacity<MODE_COOP, NT, KG>())) {
         hipLaunchKernelGGL((adam8_kernel<MODE_COOP, NT, KG>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    if (max_nparts > 1 && mode == RS_SPLIT_ORDERED &&
+        ordered_ok(max_nparts, coop_capacity<MODE_ORDERED, NT, KG>())) {
+        hipLaunchKernelGGL((adam8_kernel<MODE_ORDERED, NT, KG>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     if (max_nparts > 1) {
@@ -558,8 +611,10 @@ hipError_t launch_nt(const StepArgs& a, int32_t mode, int32_t max_nparts, hipStr
 // Lanes own 16 elements: fewer, larger workgroups amortise the per-chunk
 // reduction and the cross-workgroup wait better than more waves with less
 // work each.
+constexpr int kStepKG = 4;
+
 StepGeometry step_geometry(int64_t chunk_elems) {
-    const int kg = 4;
+    const int kg = kStepKG;
     const int64_t lanes = (chunk_elems + 4 * kg - 1) / (4 * kg);
     int nt = 64;
     while (nt < lanes && nt < kMaxStepThreads) nt *= 2;
@@ -584,15 +639,15 @@ hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const 
     const StepGeometry g = step_geometry(chunk_elems);
     switch (g.threads) {
     case 64:
-        return launch_nt<64, 4>(a, mode, max_nparts, s);
+        return launch_nt<64, kStepKG>(a, mode, max_nparts, s);
     case 128:
-        return launch_nt<128, 4>(a, mode, max_nparts, s);
+        return launch_nt<128, kStepKG>(a, mode, max_nparts, s);
     case 256:
-        return launch_nt<256, 4>(a, mode, max_nparts, s);
+        return launch_nt<256, kStepKG>(a, mode, max_nparts, s);
     case 512:
-        return launch_nt<512, 4>(a, mode, max_nparts, s);
+        return launch_nt<512, kStepKG>(a, mode, max_nparts, s);
     default:
-        return launch_nt<1024, 4>(a, mode, max_nparts, s);
+        return launch_nt<1024, kStepKG>(a, mode, max_nparts, s);
     }
 }
 

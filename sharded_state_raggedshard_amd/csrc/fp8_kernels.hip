@@ -17,6 +17,7 @@
 // 16 elements per lane as four 4-element groups, as in the step.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <mutex>
 
 #include "kernel_common.hpp"
@@ -109,23 +110,34 @@ __device__ void zero_bytes(uint8_t* p, int64_t n) {
     for (int64_t i = head + 16 * nv + threadIdx.x; i < n; i += NT) p[i] = 0;
 }
 
-// Whole block of any shape, two sweeps (absmax, then codes).
+// Whole block of any shape, two sweeps (absmax, then codes), element by
+// element over its pieces ds[0 .. nd) (all in one tensor, whose bound view
+// starts at buffer position tstart).
 template <int NT>
-__device__ void fp8_scalar_chunk(const ChunkDesc& d, const float* src, uint8_t* buf, float* scale,
-                                 float* red) {
-    const int64_t n = int64_t(d.rows) * d.cols;
+__device__ void fp8_block_sweeps(const ChunkDesc* ds, int nd, const float* view, int64_t tstart,
+                                 uint8_t* buf, float* scale, float* red) {
     float am = 0.0f, dummy = 0.0f;
-    for (int64_t e = threadIdx.x; e < n; e += NT) {
-        const int64_t r = e / d.cols, off = r * d.ld + (e - r * d.cols);
-        am = fmaxf(am, fabsf(src[off]));
+    for (int q = 0; q < nd; ++q) {
+        const ChunkDesc d = ds[q];
+        const float* src = view + (d.pos - tstart);
+        const int64_t n = int64_t(d.rows) * d.cols;
+        for (int64_t e = threadIdx.x; e < n; e += NT) {
+            const int64_t r = e / d.cols, off = r * d.ld + (e - r * d.cols);
+            am = fmaxf(am, fabsf(src[off]));
+        }
     }
     wg_max2<NT>(am, dummy, red);
     const float s = am / 448.0f, y = quant_recip(s);
-    for (int64_t e = threadIdx.x; e < n; e += NT) {
-        const int64_t r = e / d.cols, off = r * d.ld + (e - r * d.cols);
-        buf[d.pos + off] = (uint8_t)fp8_of(src[off], s, y);
+    for (int q = 0; q < nd; ++q) {
+        const ChunkDesc d = ds[q];
+        const float* src = view + (d.pos - tstart);
+        const int64_t n = int64_t(d.rows) * d.cols;
+        for (int64_t e = threadIdx.x; e < n; e += NT) {
+            const int64_t r = e / d.cols, off = r * d.ld + (e - r * d.cols);
+            buf[d.pos + off] = (uint8_t)fp8_of(src[off], s, y);
+        }
     }
-    if (threadIdx.x == 0) scale[d.blk] = s;
+    if (threadIdx.x == 0) scale[ds[0].blk] = s;
 }
 
 // A run of single-element blocks: each element is its own block.
@@ -139,12 +151,11 @@ __device__ void fp8_elem_chunk(const ChunkDesc& d, const float* src, uint8_t* bu
     }
 }
 
+// Codes (and scale) of one chunk.
 template <int MODE, int NT>
-__global__ __launch_bounds__(NT) void fp8_pack_kernel(Fp8Args a) {
+__device__ __forceinline__ void fp8_pack_chunk(const Fp8Args& a, int64_t c, const ChunkDesc& d,
+                                               float* red) {
     constexpr int KG = kPackKG, WSPAN = 256 * KG;
-    __shared__ float red[2 * (NT / 64) + 2];
-    const int64_t c = chunk_of(a.r, blockIdx.x);
-    const ChunkDesc d = a.b.chunks[c];
     const bool split = d.nparts > 1;
     if (MODE == MODE_PARTIAL && (d.kind != KIND_VEC || !split)) return;
     if (d.kind == KIND_PAD) {
@@ -154,7 +165,9 @@ __global__ __launch_bounds__(NT) void fp8_pack_kernel(Fp8Args a) {
     const int j = tensor_at(a.tt, d.pos);
     const float* src = reinterpret_cast<const float*>(a.tt.views[j]) + (d.pos - a.tt.tstart[j]);
     if (d.kind == KIND_SCALAR) {
-        if (MODE != MODE_PARTIAL) fp8_scalar_chunk<NT>(d, src, a.b.buf, a.b.scale, red);
+        if (MODE != MODE_PARTIAL)
+            fp8_block_sweeps<NT>(a.b.chunks + c, 1, reinterpret_cast<const float*>(a.tt.views[j]),
+                                 a.tt.tstart[j], a.b.buf, a.b.scale, red);
         return;
     }
     if (d.kind == KIND_ELEM) {
@@ -222,6 +235,56 @@ __global__ __launch_bounds__(NT) void fp8_pack_kernel(Fp8Args a) {
     if (threadIdx.x == 0 && d.part == 0) a.b.scale[d.blk] = s;
 }
 
+// One workgroup per chunk.  MODE_PARTIAL / MODE_MAIN: the two launches of
+// the two-pass split; MODE_COOP / MODE_ORDERED: one launch, split blocks
+// meeting on the cooperative slots, the chunk taken as in the step's kernel
+// (workgroup index, or a counter), with the same wait-free whole-block path
+// while the device status word is set.
+template <int MODE, int NT>
+__global__ __launch_bounds__(NT) void fp8_pack_kernel(Fp8Args a) {
+    constexpr bool kCoop = MODE == MODE_COOP || MODE == MODE_ORDERED;
+    __shared__ float red[2 * (NT / 64) + 2];
+    __shared__ uint32_t status;
+    __shared__ int64_t taken;
+    // the chunk descriptor is read before the barrier where the chunk is known
+    // (its latency overlaps the status word's)
+    int64_t c = 0;
+    ChunkDesc d;
+    if (MODE != MODE_ORDERED) {
+        c = chunk_of(a.r, blockIdx.x);
+        d = a.b.chunks[c];
+    }
+    if (kCoop) {
+        if (threadIdx.x == 0) {
+            CoopCounters* k = a.b.counters;
+            status = __hip_atomic_load(&k->timeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (MODE == MODE_ORDERED) {
+                const uint32_t t = __hip_atomic_fetch_add(&k->claim[0], 1u, __ATOMIC_RELAXED,
+                                                          __HIP_MEMORY_SCOPE_AGENT);
+                if ((int64_t)t + 1 == a.nwg)
+                    __hip_atomic_store(&k->claim[0], 0u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+                taken = t;
+            }
+        }
+        __syncthreads();
+    }
+    if (MODE == MODE_ORDERED) {
+        c = chunk_of(a.r, taken);
+        d = a.b.chunks[c];
+    }
+    if (kCoop && status != 0u && d.kind == KIND_VEC && d.nparts > 1 && d.run_log2 < 0) {
+        if (d.part == 0) {
+            const int j = tensor_at(a.tt, d.pos);
+            fp8_block_sweeps<NT>(a.b.chunks + c, d.nparts,
+                                 reinterpret_cast<const float*>(a.tt.views[j]), a.tt.tstart[j],
+                                 a.b.buf, a.b.scale, red);
+        }
+        return;
+    }
+    fp8_pack_chunk<kCoop ? MODE_COOP : MODE, NT>(a, c, d, red);
+}
+
 // Copy-out: bf16(e4m3(code) * s) into the bound bf16 views.
 template <int NT>
 __global__ __launch_bounds__(NT) void fp8_unpack_kernel(Fp8Args a) {
@@ -269,7 +332,7 @@ __global__ __launch_bounds__(NT) void fp8_unpack_kernel(Fp8Args a) {
     }
 }
 
-template <int NT>
+template <int MODE, int NT>
 int fp8_coop_capacity() {
     static std::mutex mu;
     static int cached[64] = {0};
@@ -279,7 +342,7 @@ int fp8_coop_capacity() {
     if (cached[dev] == 0) {
         int per_cu = 0, ncu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(fp8_pack_kernel<MODE_COOP, NT>), NT, 0) !=
+                &per_cu, reinterpret_cast<const void*>(fp8_pack_kernel<MODE, NT>), NT, 0) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -312,10 +375,14 @@ hipError_t launch_pack_fp8(const Ranges& chunk_ranges, const Fp8Buffers& b, cons
     if (a.nwg == 0) return hipSuccess;
     if (a.nwg > 0x7fffffffLL) return hipErrorInvalidValue;
     const dim3 grid((unsigned)a.nwg), block(NT);
-    // cooperative only with a 2x margin on residency, as in the step
     if (max_nparts > 1 && mode == RS_SPLIT_COOPERATIVE &&
-        2 * (int64_t)max_nparts <= fp8_coop_capacity<NT>()) {
+        coop_ok(max_nparts, fp8_coop_capacity<MODE_COOP, NT>())) {
         hipLaunchKernelGGL((fp8_pack_kernel<MODE_COOP, NT>), grid, block, 0, s, a);
+        return hipGetLastError();
+    }
+    if (max_nparts > 1 && mode == RS_SPLIT_ORDERED &&
+        ordered_ok(max_nparts, fp8_coop_capacity<MODE_ORDERED, NT>())) {
+        hipLaunchKernelGGL((fp8_pack_kernel<MODE_ORDERED, NT>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     if (max_nparts > 1) {

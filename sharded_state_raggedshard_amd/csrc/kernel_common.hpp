@@ -11,7 +11,30 @@
 namespace rs {
 namespace kc {
 
-enum { MODE_PARTIAL = 0, MODE_MAIN = 1, MODE_COOP = 2 };
+enum { MODE_PARTIAL = 0, MODE_MAIN = 1, MODE_COOP = 2, MODE_ORDERED = 3 };
+
+// When a one-launch split mode is safe, given the most chunks P of any block
+// and the workgroups `capacity` of the kernel the device holds at once.
+//
+// MODE_ORDERED: chunks are taken from a counter in increasing order, so at
+// most P - 1 workgroups can wait on chunks not yet taken (all in the block
+// straddling the counter); a device holding more than P workgroups always
+// has room for one more.  Asked here with a factor 2 margin, for kernels of
+// other streams that may share the device.
+inline bool ordered_ok(int64_t P, int64_t capacity) { return capacity >= 2 * P; }
+
+// MODE_COOP: workgroup w takes chunk w.  gfx950 starts the workgroups of a
+// launch on its 8 XCDs in turn and in index order on each XCD.  A wait can
+// then only stall for good if every workgroup resident on one XCD waits for
+// a chunk that XCD has not started; those have indices in (w - P, w) for
+// the first such chunk w, at most ceil(P / 8) of them, so an XCD holding
+// more than ceil(P / 8) workgroups cannot stall.  Asked here with a factor 2
+// margin: capacity / 8 >= 2 ceil(P / 8).  (HIP does not promise this start
+// order; RS_SPLIT_ORDERED needs no such promise.)
+constexpr int kXcds = 8;
+inline bool coop_ok(int64_t P, int64_t capacity) {
+    return capacity >= 2 * kXcds * ((P + kXcds - 1) / kXcds) && capacity >= 2 * P;
+}
 
 
 // Bounded wait for the other chunks of a block (tens of ms of sleeps; a

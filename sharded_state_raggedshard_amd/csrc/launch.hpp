@@ -67,9 +67,10 @@ struct StepBuffers {
     CoopCounters* counters;
 };
 
-// Chunk-index ranges [lo, hi) of the chunk table; mode RS_SPLIT_*.  The
-// cooperative mode is used only when max_nparts chunks of one block are
-// sure to be resident together; otherwise the launch falls back to two-pass.
+// Chunk-index ranges [lo, hi) of the chunk table; mode RS_SPLIT_*.  A
+// one-launch mode is used only when the device holds enough workgroups of
+// the kernel for max_nparts (kc::coop_ok, kc::ordered_ok); otherwise the
+// launch falls back to two-pass.
 hipError_t launch_adam8(const Ranges& chunk_ranges, const StepBuffers& b, const StepScalars& sc,
                         int32_t mode, int64_t chunk_elems, int32_t max_nparts, hipStream_t s);
 

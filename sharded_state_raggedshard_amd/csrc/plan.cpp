@@ -637,7 +637,7 @@ rs_status build_tables(Plan& p, std::string& err) {
     p.off_l2 = off;
     off = align256(off + size_t(kL2Blocks) * 8);
     p.off_flag = off;
-    off = align256(off + 16);
+    off = align256(off + sizeof(CoopCounters));
     p.ws_bytes = off;
     p.tables_built = true;
     return RS_OK;

@@ -51,11 +51,17 @@ struct alignas(16) PartSlot {
     uint64_t v;
 };
 
-// Device status of the cooperative step.
-struct alignas(16) CoopCounters {
+// Device words of the one-launch split modes: the status word, and the
+// chunk counter of RS_SPLIT_ORDERED launches (claim[0]; the workgroup that
+// takes a launch's last chunk zeroes it for the next launch; claim[1] is
+// unused).  The counter sits on its own 128-byte line.
+struct alignas(256) CoopCounters {
     uint32_t timeout;  // set when a bounded wait gave up
-    uint32_t pad[3];
+    uint32_t pad0[31];
+    uint32_t claim[2];
+    uint32_t pad1[30];
 };
+static_assert(sizeof(CoopCounters) == 256, "CoopCounters layout");
 static_assert(sizeof(PartSlot) == 16, "PartSlot layout");
 
 constexpr int kVecAlign = 4;         // vector width (elements) of the step kernel

@@ -177,6 +177,7 @@ def test_invalid_specs_and_arguments():
     _expect(rs.RS_ESTATE, rs.rs_adam8_step, h, 0, 0, fake, fake, fake, fake, fake, fake, stream=0)
     _expect(rs.RS_ESTATE, rs.rs_bind_views, h, rs.RS_VIEW_F32_SRC, [fake], stream=0)
     _expect(rs.RS_ESTATE, rs.rs_plan_check_device, h, stream=0)
+    _expect(rs.RS_ESTATE, rs.rs_plan_status_offset, h)
     # selection and pointer checks
     _expect(rs.RS_EINVAL, rs.rs_pack_shard, h, 3, 0, fake, stream=0)
     _expect(rs.RS_EINVAL, rs.rs_pack_shard, h, 0, 5, fake, stream=0)

@@ -67,7 +67,8 @@ def _check_pack(L, plan, hv, dv, bucket, rank):
     return buf, sc
 
 
-@pytest.mark.parametrize("mode", [rs.RS_SPLIT_TWO_PASS, rs.RS_SPLIT_COOPERATIVE])
+@pytest.mark.parametrize("mode", [rs.RS_SPLIT_TWO_PASS, rs.RS_SPLIT_COOPERATIVE,
+                                  rs.RS_SPLIT_ORDERED])
 @pytest.mark.parametrize("name", list(CASES))
 def test_fp8_pack_unpack_bitexact(name, mode):
     specs, m, g = CASES[name]()
@@ -90,7 +91,7 @@ def test_fp8_pack_unpack_bitexact(name, mode):
     L.unpack_fp8(-1, hexp, buf.cpu().numpy(), sc.cpu().numpy())
     for s, o, e in zip(specs, outs, hexp):
         assert np.array_equal(dev_to_u16(o), e), s.name
-    if mode == rs.RS_SPLIT_COOPERATIVE:
+    if mode != rs.RS_SPLIT_TWO_PASS:
         rs.rs_plan_check_device(plan.h)
     plan.free()
 
@@ -173,5 +174,31 @@ def test_fp8_full_size_sampled_blocks(w):
         got = buf[torch.from_numpy(P).cuda()].cpu().numpy()
         assert np.array_equal(got, q), (t, k)
         assert np.float32(sc[L.blk0[t] + k].item()) == np.float32(s)
+    rs.rs_plan_check_device(plan.h)
+    plan.free()
+
+
+@pytest.mark.parametrize("mode", [rs.RS_SPLIT_COOPERATIVE, rs.RS_SPLIT_ORDERED])
+def test_fp8_status_word_set_takes_wait_free_path_exactly(mode):
+    """With the device status word set before the launch, the one-launch
+    FP8 copy-in encodes every split block whole in one workgroup (no wait):
+    codes and scales stay bit-exact, and rs_plan_check_device reports and
+    clears the word."""
+    specs, m, g = CASES["kinds"]()
+    log(f"fp8 status word fallback mode={mode}")
+    L = oracle.Layout(specs, m, g)
+    plan = make_plan(specs, m, g, mode=mode)
+    hv = _views(specs, 11)
+    dv = [torch.from_numpy(v).cuda() for v in hv]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, dv)
+    off = rs.rs_plan_status_offset(plan.h)
+    for rank in (rs.RS_ALL, 0, m - 1):
+        torch.cuda.synchronize()
+        plan.workspace[off:off + 4].view(torch.int32).fill_(1)
+        _check_pack(L, plan, hv, dv, rs.RS_ALL, rank)
+        with pytest.raises(rs.RaggedShardError) as ei:
+            rs.rs_plan_check_device(plan.h)
+        assert ei.value.status == rs.RS_EHIP
+    _check_pack(L, plan, hv, dv, rs.RS_ALL, rs.RS_ALL)
     rs.rs_plan_check_device(plan.h)
     plan.free()

@@ -134,7 +134,8 @@ def test_llama8b_tiles_ranks_0_and_43(mode):
     plan.free()
 
 
-@pytest.mark.parametrize("mode", [rs.RS_SPLIT_TWO_PASS, rs.RS_SPLIT_COOPERATIVE])
+@pytest.mark.parametrize("mode", [rs.RS_SPLIT_TWO_PASS, rs.RS_SPLIT_COOPERATIVE,
+                                  rs.RS_SPLIT_ORDERED])
 def test_moe_bucket_ranks_0_and_46_warm(mode):
     """Fused-expert MoE bucket, 48 ranks, 128-row blocks of 368,640
     elements (23 chunks each), warm states, steps 11 and 12."""
@@ -147,7 +148,7 @@ def test_moe_bucket_ranks_0_and_46_warm(mode):
     for rank in (0, 46):
         bi, bo = _sample_blocks(L, rank, 6, rng)
         _run(L, plan, [(0, rank)], [11, 12], bi, bo, seed=0, sigma=1e-3, warm=True)
-    if mode == rs.RS_SPLIT_COOPERATIVE:
+    if mode != rs.RS_SPLIT_TWO_PASS:
         rs.rs_plan_check_device(plan.h)
     plan.free()
 

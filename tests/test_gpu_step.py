@@ -14,7 +14,7 @@ from gpu_harness import (SENT_CODE, DevState, assert_step_close, check_plan_matc
 
 pytestmark = pytest.mark.gpu
 
-TWO, COOP = rs.RS_SPLIT_TWO_PASS, rs.RS_SPLIT_COOPERATIVE
+TWO, COOP, ORD = rs.RS_SPLIT_TWO_PASS, rs.RS_SPLIT_COOPERATIVE, rs.RS_SPLIT_ORDERED
 
 
 def _mixed_specs():
@@ -88,13 +88,13 @@ def _run_free(name, mode, chunk, steps=3, per_rank=False, warm=False, gscale=Non
         out = dev_to_u16(ds.out)
         assert (out[pad] == 0).all()
         assert np.array_equal(out[~pad], oracle.bf16(got.theta[~pad]))
-    if mode == COOP:
+    if mode != TWO:
         rs.rs_plan_check_device(plan.h)
     plan.free()
     return got
 
 
-@pytest.mark.parametrize("mode", [TWO, COOP])
+@pytest.mark.parametrize("mode", [TWO, COOP, ORD])
 @pytest.mark.parametrize("chunk", [None, 1024, 64])
 @pytest.mark.parametrize("name", list(CASES))
 def test_step_free_running(name, chunk, mode):
@@ -102,7 +102,7 @@ def test_step_free_running(name, chunk, mode):
     _run_free(name, mode, chunk)
 
 
-@pytest.mark.parametrize("mode", [TWO, COOP])
+@pytest.mark.parametrize("mode", [TWO, COOP, ORD])
 def test_step_per_rank_calls_and_warm_states(mode):
     log(f"step per-rank warm mode={mode}")
     _run_free("mixed", mode, 1024, steps=2, per_rank=True, warm=True)
@@ -120,7 +120,7 @@ def test_modes_and_chunk_sizes_agree_bitwise():
     L = oracle.Layout(specs, m, g)
     hs = host_state(L, specs, seed=4, sigma=sigma, warm=True)
     results = []
-    for mode, chunk in [(TWO, None), (COOP, None), (TWO, 256), (COOP, 64)]:
+    for mode, chunk in [(TWO, None), (COOP, None), (TWO, 256), (COOP, 64), (ORD, None), (ORD, 64)]:
         plan = make_plan(specs, m, g, chunk=chunk, mode=mode)
         ds = DevState(hs, with_out=True)
         for t in (11, 12):
@@ -135,7 +135,7 @@ def test_modes_and_chunk_sizes_agree_bitwise():
             assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("mode", [TWO, COOP])
+@pytest.mark.parametrize("mode", [TWO, COOP, ORD])
 def test_llama_layer_full_parity(mode):
     """The Llama-style layer (51.4M elements, 32-row blocks, 8 ranks): two
     free-running steps over every element."""
@@ -162,7 +162,7 @@ def test_llama_layer_full_parity(mode):
         log(f"  step {t}: codes equal m={np.array_equal(got.qm, ref.qm)} "
             f"v={np.array_equal(got.qv, ref.qv)}; max |dtheta| "
             f"{np.abs(got.theta[~pad] - ref.theta[~pad]).max():.3e}")
-    if mode == COOP:
+    if mode != TWO:
         rs.rs_plan_check_device(plan.h)
     plan.free()
 
@@ -208,3 +208,52 @@ def test_step_with_planner_orders(name, options):
     """Reordered plans: tensors sit in buffer order, block ids follow it."""
     log(f"step {name} options={options:#x}")
     _run_free(name, COOP, 1024, steps=2, options=options)
+
+
+def _set_status_word(plan, value):
+    off = rs.rs_plan_status_offset(plan.h)
+    torch.cuda.synchronize()
+    plan.workspace[off:off + 4].view(torch.int32).fill_(value)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("mode", [COOP, ORD])
+@pytest.mark.parametrize("name,chunk", [("mixed", 1024), ("mixed", 64), ("multi_bucket", 64)])
+def test_status_word_set_takes_wait_free_path_exactly(name, chunk, mode):
+    """With the device status word set before the launch (as after a wait
+    that gave up), the one-launch step updates every split block whole in
+    one workgroup, with no wait: results stay those of the oracle (codes
+    exact), every kernel ends normally, and rs_plan_check_device reports and
+    clears the word; the next steps take the waiting path again."""
+    specs, m, g, sigma = CASES[name]()
+    log(f"status word fallback {name} chunk={chunk} mode={mode}")
+    L = oracle.Layout(specs, m, g)
+    plan = make_plan(specs, m, g, chunk=chunk, mode=mode)
+    hs = host_state(L, specs, seed=3, sigma=sigma, warm=True)
+    ds = DevState(hs, with_out=True)
+    ref = hs.copy()
+    ref_out = np.zeros(L.total, dtype=np.uint16)
+    pad = padding_mask(L)
+    for t in (11, 12, 13):
+        if t > 11:
+            gr = fresh_grads(L, specs, 3, sigma, t)
+            ref.grad = gr
+            ds.grad.copy_(u16_to_dev(gr))
+        if t < 13:
+            _set_status_word(plan, 1)
+        ds.step(plan, rs.RS_ALL, rs.RS_ALL, t)
+        L.adam8_step(-1, -1, ref.theta, ref.grad, ref.qm, ref.qv, ref.am, ref.av,
+                     oracle.HParams(step=t), out=ref_out)
+        got = ds.host()
+        assert_step_close(got, ref, mask=~pad, what=f"{name} step {t}")
+        assert np.array_equal(got.qm, ref.qm) and np.array_equal(got.qv, ref.qv)
+        assert np.array_equal(got.am, ref.am) and np.array_equal(got.av, ref.av)
+        assert (got.qm[pad] == SENT_CODE).all() and (got.theta[pad] == 7.0).all()
+        out = dev_to_u16(ds.out)
+        assert np.array_equal(out[~pad], oracle.bf16(got.theta[~pad]))
+        if t < 13:
+            with pytest.raises(rs.RaggedShardError) as ei:
+                rs.rs_plan_check_device(plan.h)
+            assert ei.value.status == rs.RS_EHIP
+        rs.rs_plan_check_device(plan.h)  # cleared
+    plan.free()
