@@ -1,32 +1,40 @@
 """Benchmark of the one-GPU RaggedShard / DBuffer shard-state path.
 
-One step = one pass of the whole hot path over one batch of synthetic
-gradients, in stream order on one GPU:
-    group_l2norm(grad, all slices) -> clip_coef -> adam8_step(all slices,
-    grad scale = clip coefficient) -> pack_shard(all slices, fp32 master ->
-    bf16 gathered buffer) -> unpack_full(bf16 buffer -> per-parameter views)
-    -> group_zero(the gradient accumulation buffer of the next step)
-All m simulated ranks' slices live in one device buffer (the gathered
-buffer stands in for AllGather / ReduceScatter).  Two seeded random
-gradient buffers alternate between steps, so every step reads a full
-synthetic gradient; the zeroing clears a third buffer of the same size (what
-the next backward pass would accumulate into).  Inputs are resident in HBM
-before the timed region.  Prints one JSON line.
+Headline workload: the whole Llama-8B-shaped state on one rank (8.03e9
+fp32 master parameters, 291 tensors, 32-row quantisation blocks, m = 1),
+the largest configuration that fits one GPU.  One step = one pass of the
+whole hot path over one batch of synthetic gradients, in stream order:
+    group_l2norm(grad) -> clip_coef -> adam8_step(grad scale = the clip
+    coefficient, fused bf16 copy-in into the gathered buffer) ->
+    unpack_full(gathered buffer -> per-parameter bf16 views) ->
+    group_zero(the gradient buffer the next backward pass accumulates into)
+Two seeded random gradient buffers alternate between steps, so every step
+reads a full gradient.  Inputs are resident in HBM before the timed region;
+a step streams about 200 GB, far beyond the 256 MB last-level cache, so
+nothing is served from cache.  After the K timed steps, the step without
+the fused output, the standalone copy-in (pack_shard) and the FP8 copy-in /
+copy-out are timed on their own (K calls each, HIP events).
 
-After the step, the FP8 copy-in (fp32 master -> E4M3 codes with one fp32
-scale per quantisation block) and its copy-out (codes -> bf16 views) are
-timed on their own over the same selection (`fp8_copy`; --no-fp8 skips it).
+`per_config` then times every op of the other workloads on their own
+(events around each call, 1 GiB of unrelated memory read before each timed
+call so no input is served from cache): the Llama-style layer
+(all 8 slices), ranks 0 and 43 of the 24-layer tiled model (each rank's 24
+slices; copy-out of bucket 0), ranks 0 and 46 of the fused-expert MoE bucket.
 
-With --rank R the l2norm, the step, the pack and the zeroing act on rank R's
-slices of every bucket (its ragged local shard: the per-rank work of one
-GPU in an m-GPU job), and the copy-out unpacks bucket 0 (one gathered
-bucket).  No CPU baseline is run in that mode.
+`cpu_baseline` runs the oracle (plain C) over a bounded sample of the same
+workload on the host: the tensors of one layer plus the final norm, cut
+into row-block pieces, once on one thread and once on `min(16, cpus)`
+threads (the pieces dealt out by size; the oracle code is unchanged).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama_layer] [--rank R]
+Prints one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_full]
+                    [--rank R] [--no-per-config] [--cpu-budget S]
 """
 from __future__ import annotations
 
 import argparse
+import concurrent.futures as cf
 import json
 import os
 import sys
@@ -37,7 +45,13 @@ sys.path.insert(0, ROOT)
 
 METRIC = "int8-AdamW shard step params/s + HBM GB/s (% peak); pack/unpack GB/s"
 PEAK_GBS = 8000.0  # MI355X HBM3E
+HEADLINE = "llama8b_full"
+PER_CONFIG = [("llama_layer", None), ("llama8b_tiles", 0), ("llama8b_tiles", 43), ("moe", 0),
+              ("moe", 46)]
+GEN_CHUNK = 1 << 28
 
+
+# ------------------------------------------------------------------ sizes
 
 def selection_sizes(plan, specs, rank):
     """(real elements, buffer elements, quantisation blocks) of the selected
@@ -58,28 +72,23 @@ def selection_sizes(plan, specs, rank):
     return real, buf, blocks
 
 
-def algorithmic_bytes(real, buf, total_blocks, unpack_real):
+def algorithmic_bytes(real, buf, blocks, unpack_real, unpack_blocks):
     """Bytes each op must move (not counting padding the op never touches)."""
     pad = buf - real
     return {
         # theta r/w 8, grad 2, q_m r/w 2, q_v r/w 2 per element; absmax m/v r/w per block
-        "adam8_step": 14 * real + 16 * total_blocks,
+        "adam8_step": 14 * real + 16 * blocks,
+        # the same with the fused bf16 copy-in: + bf16 write 2 per element
+        "adam8_step_bf16_out": 16 * real + 16 * blocks,
         # read fp32 4 + write bf16 2 per element; zero padding 2
         "pack_shard": 6 * real + 2 * pad,
         # read bf16 2 + write bf16 2 per element
         "unpack_full": 4 * unpack_real,
-        # read bf16 over the whole selection
+        # read / write bf16 over the whole selection
         "group_l2norm": 2 * buf,
-        # write bf16 over the whole selection
         "group_zero": 2 * buf,
-    }
-
-
-def fp8_algorithmic_bytes(real, buf, total_blocks, unpack_real, unpack_blocks):
-    """Bytes of the FP8 copy-in and copy-out (E4M3 code + fp32 scale per block)."""
-    return {
         # read fp32 4 + write code 1 per element; zero padding 1; write scale 4 per block
-        "pack_shard_fp8": 5 * real + (buf - real) + 4 * total_blocks,
+        "pack_shard_fp8": 5 * real + pad + 4 * blocks,
         # read code 1 + write bf16 2 per element; read scale 4 per block
         "unpack_full_fp8": 3 * unpack_real + 4 * unpack_blocks,
     }
@@ -103,74 +112,382 @@ def recorded_traffic(workload: str):
     return r["hbm_bytes_per_launch"]
 
 
-def cpu_baseline(w, budget_s: float):
-    """The oracle (single-threaded C) running the same hot path on a host
-    copy of the same workload, repeated until budget_s is spent."""
-    import numpy as np
+def op_entry(ms, nbytes):
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 5), "alg_bytes": int(nbytes), "GB/s": round(gbs, 1),
+            "frac": round(gbs / PEAK_GBS, 4)}
+
+
+# ------------------------------------------------------------- GPU state
+
+class Bench:
+    """Resident state of one workload selection: the plan, fp32 master, two
+    alternating bf16 gradient buffers, int8/uint8 moments, absmax arrays, the
+    gathered bf16 buffer, the next step's gradient buffer and the bf16
+    parameter views (copy-out targets)."""
+
+    def __init__(self, w, rank, dev, chunk=None, split_mode=None):
+        import torch
+
+        import sharded_state_raggedshard_amd as rs
+        import synth
+
+        self.w, self.rank, self.dev = w, rank, dev
+        mode = rs.RS_SPLIT_COOPERATIVE if split_mode is None else split_mode
+        t0 = time.perf_counter()
+        self.plan = plan = rs.Plan(w.specs, w.m, w.g_coll, chunk=chunk, split_mode=mode)
+        self.plan_s = time.perf_counter() - t0
+        plan.upload()
+        total, nblk = plan.total, plan.n_blocks
+        self.R = rs.RS_ALL if rank is None else rank
+        # the bucket(s) the copy-out unpacks: all, or bucket 0 for one rank's shard
+        self.UB = rs.RS_ALL if rank is None else 0
+        self.theta = torch.empty(total, dtype=torch.float32, device=dev)
+        self.grads = [torch.empty(total, dtype=torch.int16, device=dev) for _ in range(2)]
+        self.qm = torch.zeros(total, dtype=torch.int8, device=dev)
+        self.qv = torch.zeros(total, dtype=torch.uint8, device=dev)
+        if w.warm_states:
+            self.am = synth.random_absmax(nblk, 1e-3, w.seed, 77, device=dev)
+            self.av = synth.random_absmax(nblk, 1e-6, w.seed, 78, device=dev)
+        else:
+            self.am = torch.zeros(nblk, dtype=torch.float32, device=dev)
+            self.av = torch.zeros(nblk, dtype=torch.float32, device=dev)
+        # inputs of the selected slices (the rest of the arrays is never read)
+        if rank is None:
+            ranges = [(0, total)]
+        else:
+            ranges = [(plan.base[b] + rank * plan.S[b], plan.base[b] + (rank + 1) * plan.S[b])
+                      for b in range(plan.nb)]
+        k = 0
+        for lo, hi in ranges:
+            for a in range(lo, hi, GEN_CHUNK):
+                b = min(hi, a + GEN_CHUNK)
+                self.theta[a:b] = synth.uniform_params(b - a, w.seed, 100 + k, device=dev)
+                for j, g in enumerate(self.grads):
+                    g[a:b] = synth.normal_bf16(b - a, w.grad_sigma, w.seed + 1000 * j, 5000 + k,
+                                               device=dev).view(torch.int16)
+                if w.warm_states:
+                    self.qm[a:b] = synth.random_codes_m(b - a, w.seed, 9000 + k, device=dev)
+                    self.qv[a:b] = synth.random_codes_v(b - a, w.seed, 9500 + k, device=dev)
+                k += 1
+        self.next_grad = torch.empty(total, dtype=torch.int16, device=dev)
+        self.gathered = torch.zeros(total, dtype=torch.int16, device=dev)
+        # fp32 master views are zero-copy views of the fp32 DBuffer; the bf16
+        # views of the unpacked bucket(s) are separate tensors, the others
+        # alias the gathered buffer (skipped by the copy-out)
+        f32_views = [self.theta[plan.pos[i]:plan.pos[i] + s.numel]
+                     for i, s in enumerate(w.specs)]
+        self.bf16_views = []
+        for i, s in enumerate(w.specs):
+            if self.UB == rs.RS_ALL or int(s.bucket) == self.UB:
+                self.bf16_views.append(torch.empty(s.numel, dtype=torch.int16, device=dev))
+            else:
+                self.bf16_views.append(self.gathered[plan.pos[i]:plan.pos[i] + s.numel])
+        rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, f32_views)
+        rs.rs_bind_views(plan.h, rs.RS_VIEW_BF16_DST, self.bf16_views)
+        self.sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
+        self.scale = torch.ones(1, dtype=torch.float32, device=dev)
+        self.codes8 = torch.zeros(total, dtype=torch.uint8, device=dev)
+        self.scale8 = torch.zeros(nblk, dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream()
+        self.sid = int(self.stream.cuda_stream)
+        real, buf, blocks = selection_sizes(plan, w.specs, rank)
+        if rank is None:
+            unpack_real, unpack_blocks = real, blocks
+        else:
+            unpack_real = sum(s.numel for s in w.specs if int(s.bucket) == 0)
+            unpack_blocks = sum(rs.rs_plan_rank_blocks(plan.h, 0, r)[1] for r in range(w.m))
+        self.real, self.buf, self.blocks = real, buf, blocks
+        self.ab = algorithmic_bytes(real, buf, blocks, unpack_real, unpack_blocks)
+        self.t = w.first_step
+        torch.cuda.synchronize()
+
+    # the ops, each on torch's current stream
+    def op(self, name, t=None):
+        import sharded_state_raggedshard_amd as rs
+
+        p, R, sid = self.plan.h, self.R, self.sid
+        t = self.t if t is None else t
+        grad = self.grads[t % 2]
+        if name == "group_l2norm":
+            rs.rs_group_l2norm(p, rs.RS_ALL, R, grad, rs.RS_BF16, self.sumsq, stream=sid)
+        elif name == "clip_coef":
+            rs.rs_clip_coef(self.sumsq, 1.0, self.scale, stream=sid)
+        elif name == "adam8_step":
+            rs.rs_adam8_step(p, rs.RS_ALL, R, self.theta, grad, self.qm, self.qv, self.am, self.av,
+                             step=t, grad_scale=self.scale, stream=sid)
+        elif name == "adam8_step_bf16_out":
+            rs.rs_adam8_step(p, rs.RS_ALL, R, self.theta, grad, self.qm, self.qv, self.am, self.av,
+                             step=t, grad_scale=self.scale, bf16_out=self.gathered, stream=sid)
+        elif name == "pack_shard":
+            rs.rs_pack_shard(p, rs.RS_ALL, R, self.gathered, stream=sid)
+        elif name == "unpack_full":
+            rs.rs_unpack_full(p, self.UB, self.gathered, stream=sid)
+        elif name == "group_zero":
+            rs.rs_group_zero(p, rs.RS_ALL, R, self.next_grad, rs.RS_BF16, stream=sid)
+        elif name == "pack_shard_fp8":
+            rs.rs_pack_shard_fp8(p, rs.RS_ALL, R, self.codes8, self.scale8, stream=sid)
+        elif name == "unpack_full_fp8":
+            rs.rs_unpack_full_fp8(p, self.UB, self.codes8, self.scale8, stream=sid)
+        else:
+            raise KeyError(name)
+
+    def time_op(self, name, reps, warmup, cold=None):
+        """Average event time (ms) of `reps` calls of one op; with `cold`, a
+        1 GiB buffer is read (untimed) before every call."""
+        import torch
+
+        for _ in range(warmup):
+            self.op(name)
+            self.t += 1
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(reps)]
+        for e0, e1 in evs:
+            if cold is not None:
+                cold.sum()  # evicts the op's inputs from the caches (read only: no dirty lines)
+            e0.record(self.stream)
+            self.op(name)
+            e1.record(self.stream)
+            self.t += 1
+        torch.cuda.synchronize()
+        return sum(a.elapsed_time(b) for a, b in evs) / reps
+
+    def check(self):
+        import sharded_state_raggedshard_amd as rs
+        rs.rs_plan_check_device(self.plan.h, stream=self.sid)
+
+    def free(self):
+        import torch
+        self.plan.free()
+        for k in list(self.__dict__):
+            if k not in ("w", "ab", "real", "buf", "blocks", "plan_s", "rank"):
+                setattr(self, k, None)
+        torch.cuda.empty_cache()
+
+
+STEP_OPS = ["group_l2norm", "clip_coef", "adam8_step_bf16_out", "unpack_full", "group_zero"]
+ALONE_OPS = ["adam8_step", "pack_shard", "pack_shard_fp8", "unpack_full_fp8"]
+CONFIG_OPS = ["group_l2norm", "adam8_step", "pack_shard", "unpack_full", "group_zero",
+              "pack_shard_fp8", "unpack_full_fp8"]
+
+
+def time_steps(bn, steps, warmup):
+    """K whole steps between two synchronisations; events around every op."""
     import torch
 
-    import oracle
+    for _ in range(warmup):
+        for o in STEP_OPS:
+            bn.op(o)
+        bn.t += 1
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(STEP_OPS) + 1)]
+           for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for k in range(steps):
+        e = evs[k]
+        e[0].record(bn.stream)
+        for j, o in enumerate(STEP_OPS):
+            bn.op(o)
+            e[j + 1].record(bn.stream)
+        bn.t += 1
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    bn.check()
+    per_op = {o: sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps
+              for j, o in enumerate(STEP_OPS)}
+    ev_step = sum(e[0].elapsed_time(e[-1]) for e in evs) / steps
+    return wall * 1e3 / steps, ev_step, per_op
+
+
+def per_config(dev, reps, warmup):
+    import torch
+
     import synth
 
-    L = oracle.Layout(w.specs, w.m, w.g_coll)
-    theta = np.zeros(L.total, dtype=np.float32)
-    grads = [np.zeros(L.total, dtype=np.uint16) for _ in range(2)]
-    for i, s in enumerate(w.specs):
-        theta[L.pos[i]:L.pos[i] + s.numel] = synth.uniform_params(s.numel, w.seed, 2 * i).numpy()
-        for j, g in enumerate(grads):
-            g[L.pos[i]:L.pos[i] + s.numel] = synth.normal_bf16(
-                s.numel, w.grad_sigma, w.seed + 1000 * j, 2 * i + 1).view(
-                    torch.int16).numpy().view(np.uint16)
-    next_grad = np.zeros(L.total, dtype=np.uint16)
-    qm = np.zeros(L.total, dtype=np.int8)
-    qv = np.zeros(L.total, dtype=np.uint8)
-    am = np.zeros(L.n_blocks, dtype=np.float32)
-    av = np.zeros(L.n_blocks, dtype=np.float32)
-    buf = np.zeros(L.total, dtype=np.uint16)
-    outs = [np.zeros(s.numel, dtype=np.uint16) for s in w.specs]
-    fviews = [theta[L.pos[i]:L.pos[i] + s.numel] for i, s in enumerate(w.specs)]
-    t0 = time.perf_counter()
-    reps = 0
-    while True:
-        grad = grads[(reps + 1) % 2]
-        ss = L.group_sumsq(-1, -1, grad)
-        s = oracle.clip_coef(ss, 1.0)
-        L.adam8_step(-1, -1, theta, grad, qm, qv, am, av, oracle.HParams(step=reps + 1), gscale=s)
-        L.pack(-1, -1, fviews, buf)
-        L.unpack(-1, outs, buf)
-        L.group_zero(-1, -1, next_grad)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s:
-            break
-    real = w.real_elems
-    return {"value": real * reps / el, "unit": "params/s", "cores": 1, "kind": "oracle",
-            "sample": f"{reps} full hot-path passes (l2norm, clip, adam8 step, pack, unpack, "
-                      f"zero) of the whole {w.name} workload, {el:.1f} s, single thread"}
+    out = []
+    cold = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
+    cold.zero_()
+    for name, rank in PER_CONFIG:
+        w = synth.WORKLOADS[name]()
+        bn = Bench(w, rank, dev)
+        ops = {}
+        for o in CONFIG_OPS:
+            ms = bn.time_op(o, reps, warmup, cold=cold)
+            ops[o] = op_entry(ms, bn.ab[o])
+        bn.check()
+        out.append({"workload": w.name, "selection": "all ranks" if rank is None else
+                    f"rank {rank}, all buckets", "real_params": bn.real, "quant_blocks": bn.blocks,
+                    "m_ranks": w.m, "planner_s": round(bn.plan_s, 4),
+                    "step_params_per_s": round(bn.real / (ops["adam8_step"]["ms"] * 1e-3), 1),
+                    "ops": ops})
+        bn.free()
+        del bn
+    del cold
+    torch.cuda.empty_cache()
+    return out
 
+
+# ------------------------------------------------------------ CPU baseline
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _sample_pieces(w, piece_elems=1 << 23):
+    """The bounded sample of a workload as row-block pieces: the tensors of
+    one layer plus the final norm (or every tensor of a small workload), each
+    ROWS tensor cut into pieces of whole blocks.  A piece is its own tensor
+    spec with the same blocks, so the oracle does the same work on it."""
+    from synth import ROWS, TensorSpec
+
+    specs = [s for s in w.specs if s.name.startswith("l0.") or s.name == "final_norm"]
+    if not specs:
+        specs = list(w.specs)
+    pieces = []
+    for s in specs:
+        if s.gran != ROWS or len(s.shape) < 2:
+            pieces.append(TensorSpec(s.name, s.shape, s.gran, s.br, s.bc, 0))
+            continue
+        C = int(s.shape[-1])
+        R = s.numel // C
+        rows = max(s.br, (piece_elems // C) // s.br * s.br)
+        for r0 in range(0, R, rows):
+            pieces.append(TensorSpec(f"{s.name}[{r0}]", (min(rows, R - r0), C), ROWS, s.br, 0, 0))
+    return pieces
+
+
+class _OracleShard:
+    """One thread's pieces in an m = 1 oracle layout, with host inputs."""
+
+    def __init__(self, pieces, w, seed):
+        import numpy as np
+        import torch
+
+        import oracle
+        import synth
+
+        self.L = L = oracle.Layout(pieces, 1, w.g_coll)
+        self.theta = np.zeros(L.total, dtype=np.float32)
+        self.grads = [np.zeros(L.total, dtype=np.uint16) for _ in range(2)]
+        for i, s in enumerate(pieces):
+            p = L.pos[i]
+            self.theta[p:p + s.numel] = synth.uniform_params(s.numel, seed, 2 * i).numpy()
+            for j, g in enumerate(self.grads):
+                g[p:p + s.numel] = synth.normal_bf16(s.numel, w.grad_sigma, seed + 1000 * j,
+                                                     2 * i + 1).view(torch.int16).numpy().view(
+                                                         np.uint16)
+        self.next_grad = np.zeros(L.total, dtype=np.uint16)
+        self.qm = np.zeros(L.total, dtype=np.int8)
+        self.qv = np.zeros(L.total, dtype=np.uint8)
+        self.am = np.zeros(L.n_blocks, dtype=np.float32)
+        self.av = np.zeros(L.n_blocks, dtype=np.float32)
+        self.buf = np.zeros(L.total, dtype=np.uint16)
+        self.outs = [np.zeros(s.numel, dtype=np.uint16) for s in pieces]
+        self.fviews = [self.theta[L.pos[i]:L.pos[i] + s.numel] for i, s in enumerate(pieces)]
+        self.real = sum(s.numel for s in pieces)
+
+    def sumsq(self, t):
+        return self.L.group_sumsq(-1, -1, self.grads[t % 2])
+
+    def rest(self, t, s):
+        import oracle
+        L = self.L
+        L.adam8_step(-1, -1, self.theta, self.grads[t % 2], self.qm, self.qv, self.am, self.av,
+                     oracle.HParams(step=t), gscale=s, out=self.buf)
+        L.pack(-1, -1, self.fviews, self.buf)
+        L.unpack(-1, self.outs, self.buf)
+        L.group_zero(-1, -1, self.next_grad)
+
+
+def _cpu_leg(pieces, w, threads, budget_s):
+    import oracle
+
+    order = sorted(range(len(pieces)), key=lambda i: -pieces[i].numel)
+    bins = [[] for _ in range(threads)]
+    load = [0] * threads
+    for i in order:  # largest first onto the least-loaded thread
+        k = load.index(min(load))
+        bins[k].append(pieces[i])
+        load[k] += pieces[i].numel
+    bins = [b for b in bins if b]
+    shards = [_OracleShard(b, w, 17 + k) for k, b in enumerate(bins)]
+    real = sum(s.real for s in shards)
+
+    def one_pass(ex, t):
+        ss = sum(ex.map(lambda sh: sh.sumsq(t), shards))  # the all-reduce of the norm
+        s = oracle.clip_coef(ss, 1.0)
+        list(ex.map(lambda sh: sh.rest(t, s), shards))
+
+    with cf.ThreadPoolExecutor(max_workers=len(shards)) as ex:
+        one_pass(ex, 1)  # untimed: first touch of every page
+        t0 = time.perf_counter()
+        reps = 0
+        while True:
+            one_pass(ex, reps + 2)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget_s:
+                break
+    return real * reps / el, reps, el, real, len(shards)
+
+
+def cpu_baseline(w, budget_s: float):
+    """The oracle timed on the host over a bounded sample of the workload:
+    min(16, cpus) threads over one layer's tensors, and one thread over its
+    attention projections."""
+    pieces = _sample_pieces(w)
+    nthreads = max(1, min(16, os.cpu_count() or 1))
+    vn, repsn, eln, real, used = _cpu_leg(pieces, w, nthreads, budget_s / 2)
+    names = sorted({p.name.split("[")[0] for p in pieces})
+    what = (f"{len(names)} tensors ({real} real params: "
+            f"{'one layer and the final norm' if len(names) < len(w.specs) else 'all tensors'} "
+            f"of {w.name}) cut into {len(pieces)} row-block pieces; whole hot-path passes "
+            "(l2norm, clip, adam8 step with bf16 output, pack, unpack, zero) after one "
+            "untimed pass")
+    small = [p for p in pieces if p.name.split(".")[-1].split("[")[0] in ("q", "k", "v", "o")]
+    small = small or pieces[: max(1, len(pieces) // 4)]
+    v1, reps1, el1, real1, _ = _cpu_leg(small, w, 1, budget_s / 2)
+    return {"value": round(vn, 1), "unit": "params/s", "cores": used, "kind": "oracle",
+            "sample": f"{what}: {repsn} passes in {eln:.1f} s on {used} threads",
+            "cpu_model": _cpu_model(), "cpus": os.cpu_count(),
+            "single_thread": {"value": round(v1, 1), "unit": "params/s", "cores": 1,
+                              "sample": f"the same passes over {real1} real params (the "
+                                        f"attention projections of that layer): {reps1} passes "
+                                        f"in {el1:.1f} s on one thread"}}
+
+
+# ------------------------------------------------------------------- main
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=100)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="llama_layer")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=HEADLINE)
     ap.add_argument("--rank", type=int, default=None,
                     help="time one rank's ragged local shard instead of all m slices")
     ap.add_argument("--split-mode", default="cooperative", choices=["cooperative", "two_pass"])
     ap.add_argument("--chunk", type=int, default=None, help="elements per workgroup in the step")
-    ap.add_argument("--cpu-budget", type=float, default=12.0,
-                    help="seconds of oracle work for the CPU baseline (0 = skip)")
-    ap.add_argument("--no-fp8", action="store_true",
-                    help="skip the separate timing of the FP8 copy-in / copy-out")
+    ap.add_argument("--cpu-budget", type=float, default=16.0,
+                    help="seconds of oracle work for the CPU baseline, both legs (0 = skip)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the per-op timing of the other workloads")
     ap.add_argument("--pmc-calibration", action="store_true",
                     help="after the timed steps, copy a 1 GiB tensor once (a plain copy "
                          "kernel of known size for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the multi-GPU "
-              "path (RCCL all-gather / reduce-scatter of the planned buffers) is not part of "
-              "this build", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
+              "multi-GPU path (the RCCL all-gather / reduce-scatter of the planned buffers is "
+              "not part of it); every figure is one GPU's", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -181,148 +498,46 @@ def main():
     w = synth.WORKLOADS[args.workload]()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    mode = rs.RS_SPLIT_COOPERATIVE if args.split_mode == "cooperative" else rs.RS_SPLIT_TWO_PASS
-    t0 = time.perf_counter()
-    plan = rs.Plan(w.specs, w.m, w.g_coll, chunk=args.chunk, split_mode=mode)
-    plan_s = time.perf_counter() - t0
-    plan.upload()
-    total, nblk = plan.total, plan.n_blocks
-
-    # resident state: fp32 master, bf16 grads, int8/uint8 moments, absmax
-    theta = torch.zeros(total, dtype=torch.float32, device=dev)
-    grads = [torch.zeros(total, dtype=torch.int16, device=dev) for _ in range(2)]
-    for i, s in enumerate(w.specs):
-        p = plan.pos[i]
-        theta[p:p + s.numel] = synth.uniform_params(s.numel, w.seed, 2 * i, device=dev)
-        for j, g in enumerate(grads):
-            g[p:p + s.numel] = synth.normal_bf16(s.numel, w.grad_sigma, w.seed + 1000 * j,
-                                                 2 * i + 1, device=dev).view(torch.int16)
-    next_grad = torch.zeros(total, dtype=torch.int16, device=dev)
-    qm = torch.zeros(total, dtype=torch.int8, device=dev)
-    qv = torch.zeros(total, dtype=torch.uint8, device=dev)
-    am = torch.zeros(nblk, dtype=torch.float32, device=dev)
-    av = torch.zeros(nblk, dtype=torch.float32, device=dev)
-    gathered = torch.zeros(total, dtype=torch.int16, device=dev)
-    # fp32 master views are zero-copy views of the fp32 DBuffer; bf16
-    # parameter views are separate per-parameter tensors (copy-out target)
-    f32_views = [theta[plan.pos[i]:plan.pos[i] + s.numel] for i, s in enumerate(w.specs)]
-    bf16_views = [torch.empty(s.numel, dtype=torch.int16, device=dev) for s in w.specs]
-    rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, f32_views)
-    rs.rs_bind_views(plan.h, rs.RS_VIEW_BF16_DST, bf16_views)
-    sumsq = torch.zeros(1, dtype=torch.float64, device=dev)
-    scale = torch.ones(1, dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    sid = int(stream.cuda_stream)
-    ALL = rs.RS_ALL
-    R = ALL if args.rank is None else args.rank
-    UB = ALL if args.rank is None else 0  # bucket(s) the copy-out unpacks
     if args.rank is not None and not 0 <= args.rank < w.m:
         raise SystemExit(f"--rank must be in 0..{w.m - 1}")
-
-    ops = ["group_l2norm", "clip_coef", "adam8_step", "pack_shard", "unpack_full", "group_zero"]
-
-    def step(t, ev=None):
-        grad = grads[t % 2]
-        if ev is not None:
-            ev[0].record(stream)
-        rs.rs_group_l2norm(plan.h, ALL, R, grad, rs.RS_BF16, sumsq, stream=sid)
-        if ev is not None:
-            ev[1].record(stream)
-        rs.rs_clip_coef(sumsq, 1.0, scale, stream=sid)
-        if ev is not None:
-            ev[2].record(stream)
-        rs.rs_adam8_step(plan.h, ALL, R, theta, grad, qm, qv, am, av, step=t, grad_scale=scale,
-                         stream=sid)
-        if ev is not None:
-            ev[3].record(stream)
-        rs.rs_pack_shard(plan.h, ALL, R, gathered, stream=sid)
-        if ev is not None:
-            ev[4].record(stream)
-        rs.rs_unpack_full(plan.h, UB, gathered, stream=sid)
-        if ev is not None:
-            ev[5].record(stream)
-        rs.rs_group_zero(plan.h, ALL, R, next_grad, rs.RS_BF16, stream=sid)
-        if ev is not None:
-            ev[6].record(stream)
-
-    t = 1
-    for _ in range(args.warmup):
-        step(t)
-        t += 1
-    torch.cuda.synchronize()
-
-    # timed region: K whole steps between two synchronisations
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t_start = time.perf_counter()
-    for k in range(args.steps):
-        step(t, evs[k])
-        t += 1
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    rs.rs_plan_check_device(plan.h, stream=sid)
-
-    per_op = {o: 0.0 for o in ops}
-    step_ms = 0.0
-    for e in evs:
-        for j, o in enumerate(ops):
-            per_op[o] += e[j].elapsed_time(e[j + 1])
-        step_ms += e[0].elapsed_time(e[6])
-    per_op = {o: v / args.steps for o, v in per_op.items()}
-    ms_per_step = wall * 1e3 / args.steps
-    real, buf, sel_blocks = selection_sizes(plan, w.specs, args.rank)
-    unpack_real = real if args.rank is None else sum(
-        s.numel for s in w.specs if int(getattr(s, "bucket", 0)) == 0)
-    value = real / (ms_per_step * 1e-3)
-
-    # FP8 copy-in (E4M3 codes + one fp32 scale per block) and its bf16 copy-out,
-    # timed on their own after the step (not part of the step above)
-    fp8 = None
-    if not args.no_fp8:
-        codes = torch.zeros(total, dtype=torch.uint8, device=dev)
-        fscale = torch.zeros(nblk, dtype=torch.float32, device=dev)
-        for _ in range(max(1, args.warmup)):
-            rs.rs_pack_shard_fp8(plan.h, ALL, R, codes, fscale, stream=sid)
-            rs.rs_unpack_full_fp8(plan.h, UB, codes, fscale, stream=sid)
-        fev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-        torch.cuda.synchronize()
-        for e in fev:
-            e[0].record(stream)
-            rs.rs_pack_shard_fp8(plan.h, ALL, R, codes, fscale, stream=sid)
-            e[1].record(stream)
-            rs.rs_unpack_full_fp8(plan.h, UB, codes, fscale, stream=sid)
-            e[2].record(stream)
-        torch.cuda.synchronize()
-        rs.rs_plan_check_device(plan.h, stream=sid)
-        unpack_blocks = nblk if args.rank is None else sum(
-            rs.rs_plan_rank_blocks(plan.h, 0, r)[1] for r in range(w.m))
-        fab = fp8_algorithmic_bytes(real, buf, sel_blocks, unpack_real, unpack_blocks)
-        fp8 = {}
-        for j, o in enumerate(["pack_shard_fp8", "unpack_full_fp8"]):
-            ms = sum(e[j].elapsed_time(e[j + 1]) for e in fev) / args.steps
-            gbs = fab[o] / (ms * 1e-3) / 1e9
-            fp8[o] = {"ms": round(ms, 5), "alg_bytes": fab[o], "GB/s": round(gbs, 1),
-                      "frac": round(gbs / PEAK_GBS, 4)}
-        del codes, fscale
-
+    mode = rs.RS_SPLIT_COOPERATIVE if args.split_mode == "cooperative" else rs.RS_SPLIT_TWO_PASS
+    bn = Bench(w, args.rank, dev, chunk=args.chunk, split_mode=mode)
+    ms_per_step, ev_step, per_op = time_steps(bn, args.steps, args.warmup)
+    ops = {}
+    for o in STEP_OPS:
+        ops[o] = op_entry(per_op[o], bn.ab[o]) if o in bn.ab else {"ms": round(per_op[o], 5)}
+    for o in ALONE_OPS:  # timed on their own after the steps
+        ops[o] = op_entry(bn.time_op(o, args.steps, 2), bn.ab[o])
+    bn.check()
     if args.pmc_calibration:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev)  # 1 GiB
         dst = torch.empty_like(src)
         dst.copy_(src)
         torch.cuda.synchronize()
-
-    ab = algorithmic_bytes(real, buf, sel_blocks, unpack_real)
-    breakdown = {}
-    for o in ops:
-        d = {"ms": round(per_op[o], 5)}
-        if o in ab:
-            gbs = ab[o] / (per_op[o] * 1e-3) / 1e9
-            d.update({"alg_bytes": ab[o], "GB/s": round(gbs, 1), "frac": round(gbs / PEAK_GBS, 4)})
-        breakdown[o] = d
-    step_gbs = ab["adam8_step"] / (per_op["adam8_step"] * 1e-3) / 1e9
+        del src, dst
+    real = bn.real
+    cfg = {
+        "workload": w.name,
+        "tensors": len(w.specs),
+        "real_params": real,
+        "selection": "all ranks" if args.rank is None else f"rank {args.rank}, all buckets",
+        "m_ranks": w.m,
+        "g_coll": w.g_coll,
+        "S": bn.plan.S[0],
+        "padding": bn.plan.padding[0],
+        "quant_blocks": bn.blocks,
+        "split_mode": args.split_mode,
+        "chunk_elems": rs.rs_plan_chunk_elems(bn.plan.h),
+        "planner_s": round(bn.plan_s, 4),
+        "step": " -> ".join(STEP_OPS),
+    }
+    bn.free()
+    del bn
+    torch.cuda.empty_cache()
+    dom = ops["adam8_step_bf16_out"]
     result = {
         "metric": METRIC,
-        "value": round(value, 1),
+        "value": round(real / (ms_per_step * 1e-3), 1),
         "unit": "params/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -333,38 +548,24 @@ def main():
         "vs_baseline": None,
         "dtype": "fp32 update, int8/uint8 state, bf16 grads and copies",
         "data": "synthetic (seeded torch generators; shapes of the workload)",
-        "config": {
-            "workload": w.name,
-            "tensors": len(w.specs),
-            "real_params": real,
-            "selection": "all ranks" if args.rank is None else f"rank {args.rank}, all buckets",
-            "m_ranks": w.m,
-            "g_coll": w.g_coll,
-            "S": plan.S[0],
-            "padding": plan.padding[0],
-            "quant_blocks": sel_blocks,
-            "split_mode": args.split_mode,
-            "chunk_elems": rs.rs_plan_chunk_elems(plan.h),
-            "planner_s": round(plan_s, 4),
-        },
-        "step_params_per_s": round(real / (per_op["adam8_step"] * 1e-3), 1),
-        "ops": breakdown,
+        "config": cfg,
+        "step_params_per_s": round(real / (dom["ms"] * 1e-3), 1),
+        "ops": ops,
         "roofline": {
             "bound": "hbm",
-            "kernel": "adam8_step",
-            "achieved": round(step_gbs, 1),
+            "kernel": "adam8_step (fused bf16 output)",
+            "achieved": dom["GB/s"],
             "peak": PEAK_GBS,
             "unit": "GB/s",
-            "frac": round(step_gbs / PEAK_GBS, 4),
+            "frac": dom["frac"],
             "traffic": recorded_traffic(args.workload) if args.rank is None else None,
         },
-        "event_ms_per_step": round(step_ms / args.steps, 5),
+        "event_ms_per_step": round(ev_step, 5),
     }
-    if fp8 is not None:
-        result["fp8_copy"] = fp8
+    if not args.no_per_config:
+        result["per_config"] = per_config(dev, max(5, args.steps // 2), 2)
     if args.cpu_budget > 0 and args.rank is None:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
-    plan.free()
     print(json.dumps(result), flush=True)
 
 
