@@ -265,6 +265,22 @@ rs_status rs_group_scale(const rs_plan* plan, int32_t bucket, int32_t rank, void
 rs_status rs_group_l2norm(const rs_plan* plan, int32_t bucket, int32_t rank, const void* d_buf,
                           int32_t dtype, double* d_sumsq, void* stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, allocation-free serving or training loops, harnesses that forbid
+ * hipMalloc -- and so may not have uploaded the plan: rs_group_l2norm with
+ * the same arguments and result (the same kernels, bit for bit), but its
+ * partial sums live in the library's own device array of 2048 binary64
+ * values (16 KiB per GPU, held until the process ends) instead of the plan's
+ * workspace.  Allocates nothing and needs no rs_plan_upload.  The array
+ * holds one partial per first-pass workgroup, and the first pass never uses
+ * more than 2048 workgroups; a launch that would need more is rejected with
+ * RS_EINVAL.  Every call on one GPU shares the array: calls that overlap on
+ * one GPU (several streams, several threads) race and must be ordered by the
+ * caller.  Errors as rs_group_l2norm, and RS_EHIP if the array's device
+ * address cannot be obtained. */
+rs_status rs_group_l2norm_static(const rs_plan* plan, int32_t bucket, int32_t rank,
+                                 const void* d_buf, int32_t dtype, double* d_sumsq, void* stream);
+
 /* Gradient-clipping coefficient on the device:
  * *d_scale = (float) min(1, max_norm / (sqrt(*d_sumsq) + 1e-6)), in binary64. */
 rs_status rs_clip_coef(const double* d_sumsq, double max_norm, float* d_scale, void* stream);

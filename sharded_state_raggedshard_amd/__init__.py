@@ -35,7 +35,8 @@ EXPORTS = (
     "rs_plan_rank_blocks", "rs_plan_set_chunk", "rs_plan_set_split_mode", "rs_plan_chunk_count",
     "rs_plan_device_bytes", "rs_plan_upload", "rs_bind_views", "rs_pack_shard", "rs_unpack_full",
     "rs_pack_shard_fp8", "rs_unpack_full_fp8",
-    "rs_group_zero", "rs_group_scale", "rs_group_l2norm", "rs_clip_coef", "rs_adam8_step",
+    "rs_group_zero", "rs_group_scale", "rs_group_l2norm", "rs_group_l2norm_static",
+    "rs_clip_coef", "rs_adam8_step",
     "rs_plan_check_device", "rs_plan_status_offset", "rs_last_error", "rs_version",
 )
 
@@ -91,6 +92,7 @@ def lib() -> C.CDLL:
         "rs_group_zero": ([vp, i32, i32, vp, i32, vp], C.c_int),
         "rs_group_scale": ([vp, i32, i32, vp, i32, C.c_float, vp], C.c_int),
         "rs_group_l2norm": ([vp, i32, i32, vp, i32, vp, vp], C.c_int),
+        "rs_group_l2norm_static": ([vp, i32, i32, vp, i32, vp, vp], C.c_int),
         "rs_clip_coef": ([vp, C.c_double, vp, vp], C.c_int),
         "rs_adam8_step": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, C.POINTER(rs_adam_hparams), vp,
                            vp, vp], C.c_int),
@@ -258,6 +260,12 @@ def rs_group_l2norm(plan: int, bucket: int, rank: int, buf, dtype: int, sumsq,
                     stream=None) -> None:
     _check(lib().rs_group_l2norm(plan, bucket, rank, _ptr(buf), dtype, _ptr(sumsq),
                                  _stream(stream)))
+
+
+def rs_group_l2norm_static(plan: int, bucket: int, rank: int, buf, dtype: int, sumsq,
+                           stream=None) -> None:
+    _check(lib().rs_group_l2norm_static(plan, bucket, rank, _ptr(buf), dtype, _ptr(sumsq),
+                                        _stream(stream)))
 
 
 def rs_clip_coef(sumsq, max_norm: float, scale, stream=None) -> None:

@@ -451,6 +451,31 @@ rs_status rs_group_l2norm(const rs_plan* plan, int32_t bucket, int32_t rank, con
     return RS_OK;
 }
 
+rs_status rs_group_l2norm_static(const rs_plan* plan, int32_t bucket, int32_t rank,
+                                 const void* d_buf, int32_t dtype, double* d_sumsq, void* stream) {
+    if (!plan || !d_buf || !d_sumsq) return fail(RS_EINVAL, "NULL argument");
+    if (!aligned(d_buf, 16) || !aligned(d_sumsq, 8)) return fail(RS_EINVAL, "misaligned pointer");
+    rs_status st = check_dtype(dtype);
+    if (st != RS_OK) return st;
+    const rs::Plan& p = plan->p;
+    st = check_sel(p, bucket, rank);
+    if (st != RS_OK) return st;
+    std::vector<rs::Ranges> g = groups(elem_ranges(p, bucket, rank));
+    if (g.size() != 1) return fail(RS_EINVAL, "selection has more slices than one launch takes");
+    double* partials = nullptr;
+    int64_t capacity = 0;
+    hipError_t e = rs::l2_scratch(&partials, &capacity);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    const int64_t need = rs::l2norm_partials(g[0]);
+    if (need > capacity)
+        return fail(RS_EINVAL, "the norm needs " + std::to_string(need) +
+                                   " partial sums; the library's array holds " +
+                                   std::to_string(capacity));
+    e = rs::launch_l2norm(g[0], d_buf, dtype, partials, d_sumsq, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "l2norm launch");
+    return RS_OK;
+}
+
 rs_status rs_clip_coef(const double* d_sumsq, double max_norm, float* d_scale, void* stream) {
     if (!d_sumsq || !d_scale) return fail(RS_EINVAL, "NULL argument");
     if (!(max_norm > 0.0) || !std::isfinite(max_norm)) return fail(RS_EINVAL, "max_norm must be finite and > 0");

@@ -9,10 +9,19 @@
 // with 16-byte accesses.
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "launch.hpp"
 #include "raggedshard.h"
 
 namespace rs {
+
+// Partial sums of the allocation-free L2 norm (rs_group_l2norm_static): one
+// binary64 per workgroup of the first pass, at most kL2Blocks.  Every GPU the
+// library runs on holds its own copy until the process ends, and every call
+// on that GPU shares it.  In host code this name is only a stand-in for the
+// symbol: the device address comes from hipGetSymbolAddress (l2_scratch).
+static __device__ __align__(256) double scratch[kL2Blocks];
 
 namespace {
 
@@ -397,6 +406,33 @@ hipError_t launch_l2norm(const Ranges& r, const void* buf, int32_t dtype, double
     hipLaunchKernelGGL(sumsq_final_kernel, dim3(1), dim3(kCopyThreads), 0, s, d_partials, nwg,
                        d_out);
     return hipGetLastError();
+}
+
+hipError_t l2_scratch(double** out, int64_t* capacity) {
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static double* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        // once per device, with that device current: its copy of the array
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        addr[dev] = static_cast<double*>(p);
+    }
+    *out = addr[dev];
+    *capacity = kL2Blocks;
+    return hipSuccess;
+}
+
+int64_t l2norm_partials(const Ranges& r) {
+    Ranges rr = r;
+    const int64_t ntiles = tile_ranges(rr);
+    return std::min<int64_t>(std::max<int64_t>(ntiles, 1), kL2Blocks);
 }
 
 hipError_t launch_clip(const double* d_sumsq, double max_norm, float* d_scale, hipStream_t s) {

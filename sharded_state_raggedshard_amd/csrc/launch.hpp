@@ -47,6 +47,12 @@ hipError_t launch_l2norm(const Ranges& r, const void* buf, int32_t dtype, double
                          double* d_out, hipStream_t s);
 hipError_t launch_clip(const double* d_sumsq, double max_norm, float* d_scale, hipStream_t s);
 
+// Partial sums the L2 norm of ranges r writes (one per first-pass workgroup).
+int64_t l2norm_partials(const Ranges& r);
+// Device address (current device) and size in doubles of the library's own
+// partial-sum array for the allocation-free L2 norm.
+hipError_t l2_scratch(double** out, int64_t* capacity);
+
 // fp32 step scalars derived on the host.
 struct StepScalars {
     float beta1, beta2, omega1, omega2, eps, c_decay, step_size, kappa;
