@@ -309,6 +309,85 @@ rs_status rs_adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float
                         float* d_amax_v, const rs_adam_hparams* hp, const float* d_grad_scale,
                         uint16_t* d_bf16_out, void* stream);
 
+/* ------------------------------------------------------- distributed Muon
+ * veScale-FSDP page, section "Structure-aware training case study",
+ * distributed Muon (Algorithm 2), with the uneven per-device distribution of
+ * the "RaggedShard" section: SelectRoot picks one root rank per matrix for
+ * load balance; the matrix's update is redistributed to RaggedShard(root),
+ * the whole matrix on the root and nothing on the other ranks; the root runs
+ * Newton-Schulz; the result is redistributed back and applies to the
+ * parameters (the other ranks' Newton-Schulz is a no-op).  On one GPU every
+ * rank's region of that uneven layout lives in one "root buffer" (bf16,
+ * rs_muon_layout), next to the DBuffers of the plan.
+ * This library's reading of the update (Muon with decoupled weight decay and
+ * a per-matrix scale, as in large-scale Muon):
+ *   M <- momentum * M + g                       (binary32, DBuffer layout)
+ *   U = bf16(M)                                 (redistributed to the root)
+ *   X = U / (||U||_F + 1e-7), its transpose when R > C; five times
+ *   A = X X^T, B = b A + c A A, X = a X + B X   ((a, b, c) = (3.4445,
+ *                                                -4.7750, 2.0315); bf16
+ *                                                values, binary32 sums)
+ *   O = X (transposed back)                     (redistributed back)
+ *   theta <- theta (1 - lr wd) - (lr 0.2 sqrt(max(R, C))) O   (binary32)
+ * SelectRoot: longest processing time first on the Newton-Schulz flops
+ * 5 (4 n^2 k + 2 n^3), n = min(R, C), k = max(R, C); ties to the earlier
+ * matrix and the lower rank.  Root layout: rank by rank, each rank's
+ * matrices whole and back to back in the given order, every start a
+ * multiple of 64 elements. */
+typedef struct rs_muon rs_muon; /* opaque, host-owned */
+
+typedef struct {
+    double lr, momentum, weight_decay;
+} rs_muon_hparams;
+
+/* A Muon plan over n tensors of `plan` (indices into the plan's tensor
+ * list): each is taken as its 2-D view R x C (R, C multiples of 8, buffer
+ * offset a multiple of 8).  The plan is only read here; the Muon plan keeps
+ * what it needs.  Host only.  Errors: RS_EINVAL (bad or repeated index, a
+ * shape the kernels do not take), RS_EOVERFLOW, RS_ENOMEM. */
+rs_status rs_muon_plan(const rs_plan* plan, const int32_t* tensors, int32_t n, rs_muon** out);
+
+/* Releases a Muon plan (NULL is allowed). */
+void rs_muon_free(rs_muon* muon);
+
+/* roots[i], offsets[i]: root rank and root-buffer element offset of matrix
+ * i (given order); regions[r], r = 0..m: start of rank r's region (rank r
+ * holds [regions[r], regions[r + 1])); *root_elems: root-buffer length.
+ * Any output pointer may be NULL. */
+rs_status rs_muon_layout(const rs_muon* muon, int32_t* roots, int64_t* offsets, int64_t* regions,
+                         int64_t* root_elems);
+
+/* Device bytes of the Muon workspace: tables, per-chunk partial sums and
+ * the Newton-Schulz buffers (X, two Y, A, B per matrix, bf16). */
+size_t rs_muon_device_bytes(const rs_muon* muon);
+
+/* Copies the tables into the caller's workspace (>= rs_muon_device_bytes,
+ * 256-byte aligned); the Muon plan keeps the pointer.  Synchronises the
+ * stream.  Errors: RS_EINVAL, RS_ENOMEM (too small), RS_EHIP. */
+rs_status rs_muon_upload(rs_muon* muon, void* d_workspace, size_t bytes, void* stream);
+
+/* Momentum and redistribution to the roots, for the matrices of `root`
+ * (RS_ALL: every root): M = momentum * M + float(g) over each matrix's
+ * elements in the DBuffers d_mom (fp32) and d_grad (bf16), and
+ * d_root[offset + e] = bf16(M[pos + e]).  Errors: RS_EINVAL, RS_ESTATE (not
+ * uploaded), RS_EHIP. */
+rs_status rs_muon_gather(const rs_muon* muon, int32_t root, float* d_mom, const uint16_t* d_grad,
+                         const rs_muon_hparams* hp, uint16_t* d_root, void* stream);
+
+/* Newton-Schulz of the matrices of `root` (RS_ALL: every root), in place in
+ * the root buffer: reads U, leaves O (bf16).  Uses the workspace's buffers,
+ * so calls on one Muon plan must be stream-ordered.  Errors as
+ * rs_muon_gather. */
+rs_status rs_muon_orthogonalize(const rs_muon* muon, int32_t root, uint16_t* d_root, void* stream);
+
+/* Redistribution back and the update, for the matrices of `root` (RS_ALL:
+ * every root): theta[pos + e] = theta * (1 - lr wd) - (lr 0.2 sqrt(max(R,
+ * C))) * float(d_root[offset + e]), in binary32 (the two scalars computed in
+ * binary64 and rounded once).  d_master is the fp32 DBuffer.  Errors as
+ * rs_muon_gather. */
+rs_status rs_muon_apply(const rs_muon* muon, int32_t root, float* d_master, const uint16_t* d_root,
+                        const rs_muon_hparams* hp, void* stream);
+
 /* Synchronises the stream and reports a device-side failure of the
  * one-launch split modes: RS_EHIP if a bounded wait for the other chunks of
  * a block gave up since the last check, or if the caller set the status

@@ -38,6 +38,8 @@ EXPORTS = (
     "rs_group_zero", "rs_group_scale", "rs_group_l2norm", "rs_group_l2norm_static",
     "rs_clip_coef", "rs_adam8_step",
     "rs_plan_check_device", "rs_plan_status_offset", "rs_last_error", "rs_version",
+    "rs_muon_plan", "rs_muon_free", "rs_muon_layout", "rs_muon_device_bytes", "rs_muon_upload",
+    "rs_muon_gather", "rs_muon_orthogonalize", "rs_muon_apply",
 )
 
 
@@ -55,6 +57,10 @@ class rs_tensor_spec(C.Structure):
 class rs_adam_hparams(C.Structure):
     _fields_ = [("lr", C.c_double), ("beta1", C.c_double), ("beta2", C.c_double),
                 ("eps", C.c_double), ("weight_decay", C.c_double), ("step", C.c_int64)]
+
+
+class rs_muon_hparams(C.Structure):
+    _fields_ = [("lr", C.c_double), ("momentum", C.c_double), ("weight_decay", C.c_double)]
 
 
 _lib = None
@@ -98,6 +104,14 @@ def lib() -> C.CDLL:
                            vp, vp], C.c_int),
         "rs_plan_check_device": ([vp, vp], C.c_int),
         "rs_plan_status_offset": ([vp, C.POINTER(C.c_size_t)], C.c_int),
+        "rs_muon_plan": ([vp, P32, i32, C.POINTER(vp)], C.c_int),
+        "rs_muon_free": ([vp], None),
+        "rs_muon_layout": ([vp, P32, P64, P64, P64], C.c_int),
+        "rs_muon_device_bytes": ([vp], C.c_size_t),
+        "rs_muon_upload": ([vp, vp, C.c_size_t, vp], C.c_int),
+        "rs_muon_gather": ([vp, i32, vp, vp, C.POINTER(rs_muon_hparams), vp, vp], C.c_int),
+        "rs_muon_orthogonalize": ([vp, i32, vp, vp], C.c_int),
+        "rs_muon_apply": ([vp, i32, vp, vp, C.POINTER(rs_muon_hparams), vp], C.c_int),
         "rs_last_error": ([], C.c_char_p),
         "rs_version": ([], C.c_char_p),
     }
@@ -291,6 +305,57 @@ def rs_plan_status_offset(plan: int) -> int:
     return int(off.value)
 
 
+def rs_muon_plan(plan: int, tensors: Sequence[int]) -> int:
+    arr = (C.c_int32 * len(tensors))(*[int(t) for t in tensors])
+    h = C.c_void_p()
+    _check(lib().rs_muon_plan(plan, arr, len(tensors), C.byref(h)))
+    return h.value
+
+
+def rs_muon_free(muon: int) -> None:
+    lib().rs_muon_free(muon)
+
+
+def rs_muon_layout(muon: int, n: int, m: int):
+    """(roots, root-buffer offsets, region starts [m + 1], root-buffer length)."""
+    roots = (C.c_int32 * n)()
+    offs = (C.c_int64 * n)()
+    regs = (C.c_int64 * (m + 1))()
+    total = C.c_int64()
+    _check(lib().rs_muon_layout(muon, roots, offs, regs, C.byref(total)))
+    return list(roots), list(offs), list(regs), int(total.value)
+
+
+def rs_muon_device_bytes(muon: int) -> int:
+    return int(lib().rs_muon_device_bytes(muon))
+
+
+def rs_muon_upload(muon: int, workspace, nbytes: int, stream=None) -> None:
+    _check(lib().rs_muon_upload(muon, _ptr(workspace), nbytes, _stream(stream)))
+
+
+def _muon_hp(lr, momentum, weight_decay):
+    return rs_muon_hparams(float(lr), float(momentum), float(weight_decay))
+
+
+def rs_muon_gather(muon: int, root: int, mom, grad, root_buf, momentum: float = 0.95,
+                   stream=None) -> None:
+    hp = _muon_hp(0.0, momentum, 0.0)
+    _check(lib().rs_muon_gather(muon, root, _ptr(mom), _ptr(grad), C.byref(hp), _ptr(root_buf),
+                                _stream(stream)))
+
+
+def rs_muon_orthogonalize(muon: int, root: int, root_buf, stream=None) -> None:
+    _check(lib().rs_muon_orthogonalize(muon, root, _ptr(root_buf), _stream(stream)))
+
+
+def rs_muon_apply(muon: int, root: int, master, root_buf, lr: float = 1e-3,
+                  weight_decay: float = 0.01, stream=None) -> None:
+    hp = _muon_hp(lr, 0.0, weight_decay)
+    _check(lib().rs_muon_apply(muon, root, _ptr(master), _ptr(root_buf), C.byref(hp),
+                               _stream(stream)))
+
+
 def rs_last_error() -> str:
     return lib().rs_last_error().decode()
 
@@ -333,6 +398,38 @@ class Plan:
     def free(self):
         if self.h:
             rs_plan_free(self.h)
+            self.h = None
+        self.workspace = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass
+
+
+class Muon:
+    """Owns one rs_muon handle (distributed Muon over some tensors of a plan)
+    and, after upload, its device workspace."""
+
+    def __init__(self, plan: "Plan", tensors: Sequence[int]):
+        self.h = rs_muon_plan(plan.h, tensors)
+        self.tensors = list(tensors)
+        self.m = plan.m
+        self.roots, self.offsets, self.regions, self.root_elems = rs_muon_layout(
+            self.h, len(self.tensors), self.m)
+        self.workspace = None
+
+    def upload(self, device="cuda", stream=None):
+        import torch
+        nbytes = rs_muon_device_bytes(self.h)
+        self.workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        rs_muon_upload(self.h, self.workspace, nbytes, stream)
+        return self
+
+    def free(self):
+        if self.h:
+            rs_muon_free(self.h)
             self.h = None
         self.workspace = None
 

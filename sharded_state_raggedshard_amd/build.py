@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT = os.path.join(PKG, "libraggedshard.so")
 BUILD = os.path.join(PKG, "_build")
 
-SOURCES = ["plan.cpp", "abi.cpp", "copy_kernels.hip", "adam8_kernels.hip", "fp8_kernels.hip"]
+SOURCES = ["plan.cpp", "abi.cpp", "copy_kernels.hip", "adam8_kernels.hip", "fp8_kernels.hip",
+           "muon.cpp", "muon_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -13,10 +13,6 @@
 #include "plan.hpp"
 #include "raggedshard.h"
 
-struct rs_plan {
-    rs::Plan p;
-};
-
 namespace {
 
 thread_local std::string g_err;
@@ -145,6 +141,8 @@ rs_status check_dtype(int32_t dtype) {
 }
 
 }  // namespace
+
+rs_status rs::set_error(rs_status st, std::string msg) { return fail(st, std::move(msg)); }
 
 extern "C" {
 

@@ -1,0 +1,438 @@
+// Distributed Muon on one GPU, for gfx950.
+//
+// veScale-FSDP page, section "Structure-aware training case study",
+// distributed Muon (Algorithm 2): a root rank is chosen per matrix for load
+// balance, the matrix's update is redistributed so that the root holds all
+// of it (an uneven RaggedShard: per-rank sizes differ), Newton-Schulz runs on
+// the root, and the result goes back to the sharded layout to update the
+// parameters.  On one GPU every rank's slices live in the DBuffers and every
+// root's region in one root buffer:
+//   gather:        M <- mu M + g (binary32, in the DBuffers) and
+//                  root[off + e] = bf16(M[pos + e]);
+//   orthogonalize: X = U / (||U||_F + 1e-7) (or its transpose), then five
+//                  quintic Newton-Schulz steps A = X X^T, B = b A + c A A,
+//                  X = a X + B X as bf16 MFMA products with binary32
+//                  accumulation, every stored value bf16; the result goes
+//                  back into the root buffer;
+//   apply:         theta <- theta (1 - lr wd) - (lr 0.2 sqrt(max(R, C))) O.
+// The products are dense contractions, so they run on the matrix cores
+// (v_mfma_f32_32x32x16_bf16).  Every product is written as C = P Q^T with P
+// and Q read along their rows: A = X X^T and B = c A A^T + b A directly (A
+// is symmetric), and the update as Y' = a Y + Y B^T on Y = X^T (B is
+// symmetric), whose tiles are also stored transposed as the next X.
+#include <hip/hip_runtime.h>
+
+#include "muon.hpp"
+
+namespace rs {
+namespace mu {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// bf16 bits of x, round to nearest even; NaN -> quiet NaN with its sign.
+__device__ __forceinline__ uint32_t bf16_bits(float x) {
+    const uint32_t u = __float_as_uint(x);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) & 0x8000u) | 0x7fc0u;
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ float bf16_val(uint32_t h) { return __uint_as_float(h << 16); }
+
+// Sum over the workgroup in a fixed order (result in thread 0).
+template <int NT>
+__device__ __forceinline__ double wg_sum(double v, double* red) {
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off, 64);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double s = 0.0;
+    if (threadIdx.x == 0)
+        for (int w = 0; w < NT / 64; ++w) s += red[w];
+    return s;
+}
+
+// Index i in [i0, i1) with pre[i] <= t < pre[i + 1] (pre ascending).
+__device__ __forceinline__ int find_mat(const int64_t* pre, int i0, int i1, int64_t t) {
+    int lo = i0, hi = i1 - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (pre[mid] <= t)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+// ------------------------------------------------------------ gather
+
+constexpr int kVT = 256;  // threads of the gather / apply kernels: 8192 = 256 x 4 x 8
+
+__global__ __launch_bounds__(kVT) void gather_kernel(Tables t, int64_t c0, float* __restrict__ mom,
+                                                     const uint16_t* __restrict__ grad, float mu,
+                                                     uint16_t* __restrict__ root) {
+    const MuonChunk ch = t.chunks[c0 + blockIdx.x];
+    const MuonMat& m = t.mats[ch.mat];
+    const int64_t pos = m.pos + ch.e0, ro = m.root_off + ch.e0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int e = (v * kVT + (int)threadIdx.x) * 8;
+        if (e < ch.count) {
+            const uint4 gw = *reinterpret_cast<const uint4*>(grad + pos + e);
+            float4* mp = reinterpret_cast<float4*>(mom + pos + e);
+            const float4 a = mp[0], b = mp[1];
+            const uint32_t g2[4] = {gw.x, gw.y, gw.z, gw.w};
+            float mv[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+            uint32_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float g = bf16_val((g2[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                mv[j] = (mu * mv[j]) + g;
+                h[j] = bf16_bits(mv[j]);
+            }
+            mp[0] = make_float4(mv[0], mv[1], mv[2], mv[3]);
+            mp[1] = make_float4(mv[4], mv[5], mv[6], mv[7]);
+            *reinterpret_cast<uint4*>(root + ro + e) =
+                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                           h[6] | (h[7] << 16));
+        }
+    }
+}
+
+// ----------------------------------------------------------------- norm
+
+// Sum of squares of one chunk of U (binary64), the per-matrix total taken
+// by the prepare kernel in a fixed order.
+__global__ __launch_bounds__(kVT) void norm_kernel(Tables t, int64_t c0,
+                                                   const uint16_t* __restrict__ root) {
+    __shared__ double red[kVT / 64];
+    const MuonChunk ch = t.chunks[c0 + blockIdx.x];
+    const MuonMat& m = t.mats[ch.mat];
+    const int64_t ro = m.root_off + ch.e0;
+    double acc = 0.0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int e = (v * kVT + (int)threadIdx.x) * 8;
+        if (e < ch.count) {
+            const uint4 w = *reinterpret_cast<const uint4*>(root + ro + e);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double u = (double)bf16_val((ww[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                acc += u * u;
+            }
+        }
+    }
+    const double s = wg_sum<kVT>(acc, red);
+    if (threadIdx.x == 0) t.partials[c0 + blockIdx.x] = s;
+}
+
+// ------------------------------------------------------------- prepare
+
+// X0 = bf16(U / s) (U's transpose when R > C) and Y0 = X0^T, one 64 x 64
+// tile of U per workgroup; s = sqrt(sum of the matrix's chunk sums) + 1e-7.
+// The quotient is the binary64 one, rounded to binary32 and then to bf16.
+__global__ __launch_bounds__(256) void prep_kernel(Tables t, int32_t i0, int32_t i1,
+                                                   const uint16_t* __restrict__ root) {
+    constexpr int T = kPrepTile;
+    __shared__ double red[4];
+    __shared__ double s_sh;
+    __shared__ uint16_t tileT[T][T + 8];
+    const int64_t* pre = t.tiles;
+    const int64_t tg = pre[i0] + blockIdx.x;
+    const int i = find_mat(pre, i0, i1, tg);
+    const MuonMat& m = t.mats[i];
+    double part = 0.0;
+    for (int64_t q = threadIdx.x; q < m.gn; q += 256) part += t.partials[m.g0 + q];
+    const double tot = wg_sum<256>(part, red);
+    if (threadIdx.x == 0) s_sh = sqrt(tot) + kNsEps;
+    __syncthreads();
+    const double s = s_sh;
+    const int64_t local = tg - pre[i];
+    const int64_t tcols = (m.C + T - 1) / T;
+    const int64_t r0 = (local / tcols) * T, cc0 = (local % tcols) * T;
+    // straight copy: rows of U -> rows of X (R <= C) or of Y (R > C)
+    uint16_t* straight = t.ws + (m.tr ? m.y0 : m.x);
+    uint16_t* trans = t.ws + (m.tr ? m.x : m.y0);
+    const uint16_t* u = root + m.root_off;
+    for (int v = 0; v < 2; ++v) {
+        const int idx = v * 256 + (int)threadIdx.x;
+        const int row = idx >> 3, cv = (idx & 7) * 8;
+        const int64_t r = r0 + row, c = cc0 + cv;
+        if (r < m.R && c < m.C) {
+            const uint4 w = *reinterpret_cast<const uint4*>(u + r * m.C + c);
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            uint32_t h[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const double x = (double)bf16_val((ww[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                h[j] = bf16_bits((float)(x / s));
+                tileT[cv + j][row] = (uint16_t)h[j];
+            }
+            *reinterpret_cast<uint4*>(straight + r * m.C + c) =
+                make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                           h[6] | (h[7] << 16));
+        }
+    }
+    __syncthreads();
+    // transposed copy: column c of the tile -> row c of the transposed buffer (row length R)
+    for (int v = 0; v < 2; ++v) {
+        const int idx = v * 256 + (int)threadIdx.x;
+        const int col = idx >> 3, rv = (idx & 7) * 8;
+        const int64_t c = cc0 + col, r = r0 + rv;
+        if (c < m.C && r < m.R) {
+            uint32_t w[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[j] = (uint32_t)tileT[col][rv + 2 * j] | ((uint32_t)tileT[col][rv + 2 * j + 1] << 16);
+            *reinterpret_cast<uint4*>(trans + c * m.R + r) = make_uint4(w[0], w[1], w[2], w[3]);
+        }
+    }
+}
+
+// ------------------------------------------------------- the products
+
+constexpr int BM = kGemmTile, BN = kGemmTile, BK = 64, GT = 256;
+constexpr int LDSR = BK + 8;  // bf16 per LDS row: 16 bytes of padding against bank conflicts
+
+struct GemmArgs {
+    Tables t;
+    int32_t i0, i1;
+    int32_t kind;  // G_GRAM, G_POLY, G_UPDATE
+    int32_t it;    // Newton-Schulz step (selects the Y buffers)
+    int32_t last;  // last step: the result goes to the root buffer
+    uint16_t* root;
+};
+
+// One 128 x 128 tile of C = alpha P Q^T + beta R (P: M x K, Q: N x K, R and
+// C: M x N, all row-major bf16), stored straight (Cs) and/or transposed
+// (Ct).  Four waves, each a 64 x 64 quarter as 2 x 2 MFMA tiles of 32 x 32;
+// K in steps of 64 through two LDS buffers, the next step's global loads in
+// flight while the current one is multiplied.
+__global__ __launch_bounds__(GT) void ns_gemm_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint16_t sP[2][BM * LDSR];
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BN * LDSR];
+    const int nm = g.t.nm;
+    const int64_t* pre = g.t.tiles + (int64_t)(1 + g.kind) * (nm + 1);
+    const int64_t tg = pre[g.i0] + blockIdx.x;
+    const int mi = find_mat(pre, g.i0, g.i1, tg);
+    const MuonMat& md = g.t.mats[mi];
+    uint16_t* ws = g.t.ws;
+    const int64_t yin = (g.it & 1) ? md.y1 : md.y0;
+    const int64_t yout = (g.it & 1) ? md.y0 : md.y1;
+    const uint16_t *P, *Q, *Rr = nullptr;
+    uint16_t *Cs = nullptr, *Ct = nullptr;
+    int64_t M, N, K, ldp, ldq, ldr = 0, ldc = 0, ldct = 0;
+    float alpha = 1.0f, beta = 0.0f;
+    if (g.kind == G_GRAM) {  // A = X X^T
+        P = Q = ws + md.x;
+        ldp = ldq = md.k;
+        M = N = md.n;
+        K = md.k;
+        Cs = ws + md.a;
+        ldc = md.n;
+    } else if (g.kind == G_POLY) {  // B = c A A^T + b A
+        P = Q = Rr = ws + md.a;
+        ldp = ldq = ldr = md.n;
+        M = N = K = md.n;
+        alpha = kNsC;
+        beta = kNsB;
+        Cs = ws + md.b;
+        ldc = md.n;
+    } else {  // Y' = Y B^T + a Y, stored as Y' and as X' = Y'^T
+        P = Rr = ws + yin;
+        Q = ws + md.b;
+        ldp = ldq = ldr = md.n;
+        M = md.k;
+        N = K = md.n;
+        beta = kNsA;
+        if (!g.last) {
+            Cs = ws + yout;
+            ldc = md.n;
+            Ct = ws + md.x;
+            ldct = md.k;
+        } else if (md.tr) {  // the result is Y (R x C, C = n)
+            Cs = g.root + md.root_off;
+            ldc = md.n;
+        } else {  // the result is X (R x C, C = k)
+            Ct = g.root + md.root_off;
+            ldct = md.k;
+        }
+    }
+    const int64_t ntn = (N + BN - 1) / BN;
+    const int64_t local = tg - pre[mi];
+    const int64_t m0 = (local / ntn) * BM, n0 = (local % ntn) * BN;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int lrow = tid >> 3, lk = (tid & 7) * 8;  // this thread's global-load slots
+    uint4 rp[4], rq[4];
+    auto gload = [&](int64_t k0) {
+        const int64_t kk = k0 + lk;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const int64_t pr = m0 + lrow + 32 * v, qr = n0 + lrow + 32 * v;
+            rp[v] = (pr < M && kk < K) ? *reinterpret_cast<const uint4*>(P + pr * ldp + kk)
+                                       : make_uint4(0u, 0u, 0u, 0u);
+            rq[v] = (qr < N && kk < K) ? *reinterpret_cast<const uint4*>(Q + qr * ldq + kk)
+                                       : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    auto sstore = [&](int b) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            *reinterpret_cast<uint4*>(&sP[b][(lrow + 32 * v) * LDSR + lk]) = rp[v];
+            *reinterpret_cast<uint4*>(&sQ[b][(lrow + 32 * v) * LDSR + lk]) = rq[v];
+        }
+    };
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    gload(0);
+    sstore(0);
+    __syncthreads();
+    int b = 0;
+    const int frow = lane & 31, fk = 8 * (lane >> 5);
+    for (int64_t k0 = 0; k0 < K; k0 += BK) {
+        const bool more = k0 + BK < K;
+        if (more) gload(k0 + BK);
+#pragma unroll
+        for (int kk = 0; kk < BK; kk += 16) {
+            bf16x8 fa[2], fb[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                fa[i] = *reinterpret_cast<const bf16x8*>(
+                    &sP[b][(wm * 64 + i * 32 + frow) * LDSR + kk + fk]);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                fb[j] = *reinterpret_cast<const bf16x8*>(
+                    &sQ[b][(wn * 64 + j * 32 + frow) * LDSR + kk + fk]);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j],
+                                                                        0, 0, 0);
+        }
+        if (more) sstore(b ^ 1);
+        __syncthreads();
+        b ^= 1;
+    }
+    // epilogue: lane l holds column l % 32 of a 32 x 32 tile, register r its
+    // row 8 (r / 4) + 4 (l / 32) + r % 4
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int64_t gn = n0 + wn * 64 + j * 32 + (lane & 31);
+                const int64_t gm0 = m0 + wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
+                uint32_t h[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int64_t gm = gm0 + r;
+                    float v = alpha * acc[i][j][4 * q + r];
+                    if (Rr && gm < M && gn < N) v = v + beta * bf16_val(Rr[gm * ldr + gn]);
+                    h[r] = bf16_bits(v);
+                    if (Cs && gm < M && gn < N) Cs[gm * ldc + gn] = (uint16_t)h[r];
+                }
+                if (Ct && gn < N) {
+                    if (gm0 + 3 < M) {
+                        *reinterpret_cast<uint2*>(Ct + gn * ldct + gm0) =
+                            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                    } else {
+                        for (int r = 0; r < 4; ++r)
+                            if (gm0 + r < M) Ct[gn * ldct + gm0 + r] = (uint16_t)h[r];
+                    }
+                }
+            }
+}
+
+// ---------------------------------------------------------------- apply
+
+__global__ __launch_bounds__(kVT) void apply_kernel(Tables t, int64_t c0, float* __restrict__ theta,
+                                                    const uint16_t* __restrict__ root, double lr02,
+                                                    float c_decay) {
+    const MuonChunk ch = t.chunks[c0 + blockIdx.x];
+    const MuonMat& m = t.mats[ch.mat];
+    const float scale = (float)(lr02 * m.sqmax);
+    const int64_t pos = m.pos + ch.e0, ro = m.root_off + ch.e0;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        const int e = (v * kVT + (int)threadIdx.x) * 8;
+        if (e < ch.count) {
+            const uint4 w = *reinterpret_cast<const uint4*>(root + ro + e);
+            float4* tp = reinterpret_cast<float4*>(theta + pos + e);
+            const float4 a = tp[0], b = tp[1];
+            const uint32_t ww[4] = {w.x, w.y, w.z, w.w};
+            float th[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float o = bf16_val((ww[j >> 1] >> (16 * (j & 1))) & 0xffffu);
+                th[j] = (th[j] * c_decay) - (scale * o);
+            }
+            tp[0] = make_float4(th[0], th[1], th[2], th[3]);
+            tp[1] = make_float4(th[4], th[5], th[6], th[7]);
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_gather(const Tables& t, int64_t c0, int64_t c1, float* mom, const uint16_t* grad,
+                         float mu, uint16_t* root, hipStream_t s) {
+    if (c1 <= c0) return hipSuccess;
+    hipLaunchKernelGGL(gather_kernel, dim3((unsigned)(c1 - c0)), dim3(kVT), 0, s, t, c0, mom, grad,
+                       mu, root);
+    return hipGetLastError();
+}
+
+hipError_t launch_orthogonalize(const Tables& t, const int64_t* host_tiles, int32_t i0, int32_t i1,
+                                int64_t c0, int64_t c1, uint16_t* root, hipStream_t s) {
+    if (i1 <= i0) return hipSuccess;
+    const int64_t stride = t.nm + 1;
+    auto count = [&](int which) {
+        return host_tiles[which * stride + i1] - host_tiles[which * stride + i0];
+    };
+    hipLaunchKernelGGL(norm_kernel, dim3((unsigned)(c1 - c0)), dim3(kVT), 0, s, t, c0, root);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(prep_kernel, dim3((unsigned)count(0)), dim3(256), 0, s, t, i0, i1, root);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    for (int it = 0; it < kNsSteps; ++it) {
+        for (int kind = G_GRAM; kind <= G_UPDATE; ++kind) {
+            GemmArgs a;
+            a.t = t;
+            a.i0 = i0;
+            a.i1 = i1;
+            a.kind = kind;
+            a.it = it;
+            a.last = it == kNsSteps - 1;
+            a.root = root;
+            hipLaunchKernelGGL(ns_gemm_kernel, dim3((unsigned)count(1 + kind)), dim3(GT), 0, s, a);
+            e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
+    return hipSuccess;
+}
+
+hipError_t launch_apply(const Tables& t, int64_t c0, int64_t c1, float* theta, const uint16_t* root,
+                        double lr02, float c_decay, hipStream_t s) {
+    if (c1 <= c0) return hipSuccess;
+    hipLaunchKernelGGL(apply_kernel, dim3((unsigned)(c1 - c0)), dim3(kVT), 0, s, t, c0, theta, root,
+                       lr02, c_decay);
+    return hipGetLastError();
+}
+
+}  // namespace mu
+}  // namespace rs

@@ -74,7 +74,15 @@ rs_status plan_layout(const rs_tensor_spec* specs, int32_t n, int32_t m, int64_t
 // layout for the plan's chunk size.
 rs_status build_tables(Plan& p, std::string& err);
 
+// Records the message rs_last_error() returns on this thread; returns st.
+rs_status set_error(rs_status st, std::string msg);
+
 // Earliest admissible offset of tensor t at or after e for a fixed S, or -1.
 int64_t earliest_offset(const TensorInfo& t, int32_t m, int64_t S, int64_t e);
 
 }  // namespace rs
+
+// The ABI's opaque plan handle.
+struct rs_plan {
+    rs::Plan p;
+};

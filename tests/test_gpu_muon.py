@@ -1,0 +1,202 @@
+"""GPU parity of distributed Muon against the oracle (oracle/muon.py),
+through the C-ABI.
+
+- gather (momentum and redistribution to the roots): bit-exact;
+- apply (redistribution back and update), on a root buffer the test writes:
+  bit-exact;
+- orthogonalize (Newton-Schulz on bf16 MFMA products), on a root buffer the
+  test writes: against the binary64 oracle and the oracle that rounds to
+  bf16 where the kernels store.  Tolerance, derived from the arithmetic:
+  bf16 keeps 8 significant bits (unit roundoff 2^-9); the iteration stores
+  16 rounded values per matrix, binary32 sums add a little more, and the
+  iteration damps errors in the directions it has converged -- about 1% of
+  the result's Frobenius norm in all; the tests allow 3% against binary64
+  and 2% against the bf16-storing oracle, and 6% of the largest |O| for any
+  single element;
+- per-root calls compose to the all-root call bit for bit, and touch only
+  their root's region;
+- a whole step (gather, orthogonalize, apply) against the oracle chain, the
+  parameter tolerance following from the one on O.
+Inputs are seeded and synthetic; no oracle input comes from the library."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sharded_state_raggedshard_amd as rs
+import synth
+from oracle import muon as om
+from synth import ROWS, TensorSpec
+from gpu_harness import dev_to_u16, log, make_plan, u16_to_dev
+
+pytestmark = pytest.mark.gpu
+
+LR, WD, MU = 1e-3, 0.01, 0.95
+
+
+def _ragged_specs():
+    # edge tiles of every kernel (sizes multiples of 8, not of 64 or 128), both
+    # orientations, a square matrix, a 1-D tensor that is not a Muon matrix
+    return [TensorSpec("a", (136, 200), ROWS, 8), TensorSpec("b", (200, 136), ROWS, 8),
+            TensorSpec("n", (72,), ROWS, 8), TensorSpec("c", (64, 64), ROWS, 32),
+            TensorSpec("d", (264, 520), ROWS, 8), TensorSpec("e", (520, 48), ROWS, 8)]
+
+
+CASES = {
+    "ragged_m3": lambda: (_ragged_specs(), 3, 16),
+    "llama_layer": lambda: (synth.llama_layer_2048().specs, 8, 16),
+}
+
+
+def _setup(name):
+    specs, m, g = CASES[name]()
+    L = oracle.Layout(specs, m, g)
+    plan = make_plan(specs, m, g)
+    mats = [i for i, s in enumerate(specs) if len(s.shape) == 2]
+    mu = rs.Muon(plan, mats).upload()
+    shapes = [tuple(specs[i].shape) for i in mats]
+    return specs, L, plan, mats, mu, shapes
+
+
+def _rand_bf16(n, seed, stream, sigma):
+    return synth.normal_bf16(n, sigma, seed, stream).view(torch.int16).numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_gather_bitexact(name):
+    specs, L, plan, mats, mu, shapes = _setup(name)
+    log(f"muon gather {name}")
+    g = np.zeros(L.total, np.uint16)
+    M0 = np.zeros(L.total, np.float32)
+    for k, i in enumerate(mats):
+        p, n = L.pos[i], specs[i].numel
+        g[p:p + n] = _rand_bf16(n, 1, k, 1e-3)
+        M0[p:p + n] = synth.uniform_params(n, 2, k, lo=-1e-3, hi=1e-3).numpy()
+    d_g, d_M = u16_to_dev(g), torch.from_numpy(M0.copy()).cuda()
+    root = torch.full((mu.root_elems + 64,), 0x3C3C, dtype=torch.int16, device="cuda")
+    rs.rs_muon_gather(mu.h, rs.RS_ALL, d_M, d_g, root, momentum=MU)
+    got_M, got_root = d_M.cpu().numpy(), dev_to_u16(root)
+    exp_M = M0.copy()
+    exp_root = np.full(mu.root_elems + 64, 0x3C3C, np.uint16)
+    for k, i in enumerate(mats):
+        p, n = L.pos[i], specs[i].numel
+        exp_M[p:p + n] = om.momentum(M0[p:p + n], g[p:p + n], MU)
+        exp_root[mu.offsets[k]:mu.offsets[k] + n] = oracle.bf16(exp_M[p:p + n])
+    assert np.array_equal(got_M.view(np.uint32), exp_M.view(np.uint32))
+    assert np.array_equal(got_root, exp_root)
+    mu.free()
+    plan.free()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_apply_bitexact(name):
+    specs, L, plan, mats, mu, shapes = _setup(name)
+    log(f"muon apply {name}")
+    theta = np.full(L.total, 7.0, np.float32)
+    for i, s in enumerate(specs):
+        theta[L.pos[i]:L.pos[i] + s.numel] = synth.uniform_params(s.numel, 3, i).numpy()
+    O = _rand_bf16(mu.root_elems, 4, 0, 0.05)
+    d_th = torch.from_numpy(theta.copy()).cuda()
+    rs.rs_muon_apply(mu.h, rs.RS_ALL, d_th, u16_to_dev(O), lr=LR, weight_decay=WD)
+    exp = theta.copy()
+    for k, i in enumerate(mats):
+        p, n = L.pos[i], specs[i].numel
+        R, C = shapes[k]
+        o = oracle.bf16_to_f32(O[mu.offsets[k]:mu.offsets[k] + n])
+        exp[p:p + n] = om.apply_update(theta[p:p + n], o, R, C, LR, WD)
+    assert np.array_equal(d_th.cpu().numpy().view(np.uint32), exp.view(np.uint32))
+    mu.free()
+    plan.free()
+
+
+def _fro(x):
+    return math.sqrt(float(np.sum(np.asarray(x, np.float64) ** 2)))
+
+
+def _check_O(got, U, what):
+    ref64 = om.newton_schulz5(U, bf16=False)
+    ref16 = om.newton_schulz5(U, bf16=True)
+    e64 = _fro(got - ref64) / _fro(ref64)
+    e16 = _fro(got - ref16) / _fro(ref16)
+    emax = np.abs(got - ref64).max() / np.abs(ref64).max()
+    log(f"  {what}: rel. Frobenius {e64:.2e} (binary64 oracle), {e16:.2e} (bf16 oracle), "
+        f"max {emax:.2e}")
+    assert e64 < 3e-2 and e16 < 2e-2 and emax < 6e-2, what
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_orthogonalize_against_oracle(name):
+    specs, L, plan, mats, mu, shapes = _setup(name)
+    log(f"muon orthogonalize {name}")
+    U = np.zeros(mu.root_elems, np.uint16)
+    for k, (R, C) in enumerate(shapes):
+        U[mu.offsets[k]:mu.offsets[k] + R * C] = _rand_bf16(R * C, 5, k, 1e-3)
+    root = u16_to_dev(U)
+    rs.rs_muon_orthogonalize(mu.h, rs.RS_ALL, root)
+    got = dev_to_u16(root)
+    for k, (R, C) in enumerate(shapes):
+        u = oracle.bf16_to_f32(U[mu.offsets[k]:mu.offsets[k] + R * C]).reshape(R, C)
+        o = oracle.bf16_to_f32(got[mu.offsets[k]:mu.offsets[k] + R * C]).reshape(R, C)
+        _check_O(o.astype(np.float64), u.astype(np.float64), f"{specs[mats[k]].name} {R}x{C}")
+    mu.free()
+    plan.free()
+
+
+def test_per_root_calls_compose_and_stay_in_their_region():
+    specs, L, plan, mats, mu, shapes = _setup("ragged_m3")
+    log("muon per-root calls")
+    U = np.zeros(mu.root_elems, np.uint16)
+    for k, (R, C) in enumerate(shapes):
+        U[mu.offsets[k]:mu.offsets[k] + R * C] = _rand_bf16(R * C, 6, k, 1e-3)
+    whole = u16_to_dev(U)
+    rs.rs_muon_orthogonalize(mu.h, rs.RS_ALL, whole)
+    parts = u16_to_dev(U)
+    for r in range(plan.m):
+        before = dev_to_u16(parts)
+        rs.rs_muon_orthogonalize(mu.h, r, parts)
+        after = dev_to_u16(parts)
+        lo, hi = mu.regions[r], mu.regions[r + 1]
+        assert np.array_equal(before[:lo], after[:lo]) and np.array_equal(before[hi:], after[hi:])
+    assert np.array_equal(dev_to_u16(parts), dev_to_u16(whole))
+    mu.free()
+    plan.free()
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_whole_step_against_oracle(name):
+    """gather -> orthogonalize -> apply over all roots, two free-running steps,
+    against the oracle chain (momentum exact, O within the tolerance above)."""
+    specs, L, plan, mats, mu, shapes = _setup(name)
+    log(f"muon whole step {name}")
+    theta = np.zeros(L.total, np.float32)
+    for i, s in enumerate(specs):
+        theta[L.pos[i]:L.pos[i] + s.numel] = synth.uniform_params(s.numel, 8, i).numpy()
+    M = np.zeros(L.total, np.float32)
+    d_th, d_M = torch.from_numpy(theta.copy()).cuda(), torch.from_numpy(M.copy()).cuda()
+    root = torch.zeros(mu.root_elems, dtype=torch.int16, device="cuda")
+    ref_th, ref_M = theta.copy(), M.copy()
+    for t in (1, 2):
+        g = np.zeros(L.total, np.uint16)
+        for k, i in enumerate(mats):
+            g[L.pos[i]:L.pos[i] + specs[i].numel] = _rand_bf16(specs[i].numel, 10 + t, k, 1e-3)
+        rs.rs_muon_gather(mu.h, rs.RS_ALL, d_M, u16_to_dev(g), root, momentum=MU)
+        rs.rs_muon_orthogonalize(mu.h, rs.RS_ALL, root)
+        rs.rs_muon_apply(mu.h, rs.RS_ALL, d_th, root, lr=LR, weight_decay=WD)
+        got_th = d_th.cpu().numpy()
+        for k, i in enumerate(mats):
+            p, n = L.pos[i], specs[i].numel
+            R, C = shapes[k]
+            ref_M[p:p + n] = om.momentum(ref_M[p:p + n], g[p:p + n], MU)
+            U = oracle.bf16_to_f32(oracle.bf16(ref_M[p:p + n])).reshape(R, C).astype(np.float64)
+            O = om.newton_schulz5(U, bf16=False)
+            new = om.apply_update(ref_th[p:p + n], O.reshape(-1), R, C, LR, WD)
+            # free-running: errors of earlier steps add up (the decay only shrinks them)
+            scale = LR * 0.2 * math.sqrt(max(R, C))
+            tol = t * scale * 6e-2 * np.abs(O).max() + 1e-6 * np.abs(new)
+            assert (np.abs(got_th[p:p + n] - new) <= tol).all(), (specs[i].name, t)
+            ref_th[p:p + n] = new
+        assert np.array_equal(d_M.cpu().numpy().view(np.uint32), ref_M.view(np.uint32))
+    mu.free()
+    plan.free()
