@@ -21,6 +21,11 @@ call so no input is served from cache): the Llama-style layer
 (all 8 slices), ranks 0 and 43 of the 24-layer tiled model (each rank's 24
 slices; copy-out of bucket 0), ranks 0 and 46 of the fused-expert MoE bucket.
 
+`muon` times one distributed-Muon step (gather, Newton-Schulz on every root,
+apply) over the 2-D matrices of the Llama-style layer and of one
+Llama-8B-shaped layer; the Newton-Schulz products are MFMA work, reported
+against the 2.5 PFLOP/s dense bf16 peak.
+
 `cpu_baseline` runs the oracle (plain C) over a bounded sample of the same
 workload on the host: the tensors of one layer plus the final norm, cut
 into row-block pieces, once on one thread and once on `min(16, cpus)`
@@ -48,6 +53,10 @@ PEAK_GBS = 8000.0  # MI355X HBM3E
 HEADLINE = "llama8b_full"
 PER_CONFIG = [("llama_layer", None), ("llama8b_tiles", 0), ("llama8b_tiles", 43), ("moe", 0),
               ("moe", 46)]
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+# distributed Muon: the 2-D matrices of one Llama-style layer (8 ranks) and of
+# one Llama-8B-shaped layer (64 ranks)
+MUON_CASES = [("llama_layer", 10), ("llama8b_tiles_1layer", 3)]
 GEN_CHUNK = 1 << 28
 
 
@@ -328,6 +337,84 @@ def per_config(dev, reps, warmup):
     return out
 
 
+# --------------------------------------------------------- distributed Muon
+
+def muon_tile_flops(shapes, tile=128):
+    """MFMA work the Newton-Schulz kernels do: 128 x 128 output tiles, the
+    symmetric products (A = X X^T, B = c A A + b A) on and above the
+    diagonal only; five steps."""
+    tot = 0
+    for R, C in shapes:
+        n, k = min(R, C), max(R, C)
+        tn, tk = -(-n // tile), -(-k // tile)
+        sym = tn * (tn + 1) // 2
+        tot += 5 * 2 * tile * tile * (sym * k + sym * n + tk * tn * n)
+    return tot
+
+
+def muon_bench(dev, name, reps):
+    """One distributed-Muon step over the 2-D matrices of a workload: gather
+    (momentum, redistribution to the roots), orthogonalize (Newton-Schulz on
+    every root) and apply, each timed with events over `reps` calls."""
+    import torch
+
+    import sharded_state_raggedshard_amd as rs
+    import synth
+
+    w = synth.llama8b_tiles(layers=1) if name == "llama8b_tiles_1layer" else \
+        synth.WORKLOADS[name]()
+    plan = rs.Plan(w.specs, w.m, w.g_coll).upload()
+    mats = [i for i, s in enumerate(w.specs) if len(s.shape) == 2]
+    mu = rs.Muon(plan, mats).upload()
+    shapes = [tuple(w.specs[i].shape) for i in mats]
+    real = sum(w.specs[i].numel for i in mats)
+    theta = torch.empty(plan.total, dtype=torch.float32, device=dev).uniform_(-0.1, 0.1)
+    mom = torch.zeros(plan.total, dtype=torch.float32, device=dev)
+    grad = (torch.randn(plan.total, device=dev) * 1e-3).to(torch.bfloat16).view(torch.int16)
+    root = torch.zeros(mu.root_elems, dtype=torch.int16, device=dev)
+    calls = {
+        "gather": lambda: rs.rs_muon_gather(mu.h, rs.RS_ALL, mom, grad, root, momentum=0.95),
+        "orthogonalize": lambda: rs.rs_muon_orthogonalize(mu.h, rs.RS_ALL, root),
+        "apply": lambda: rs.rs_muon_apply(mu.h, rs.RS_ALL, theta, root, lr=1e-3,
+                                          weight_decay=0.01),
+    }
+    for _ in range(2):
+        for f in calls.values():
+            f()
+    torch.cuda.synchronize()
+    ms = {}
+    for k, f in calls.items():
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            f()  # Newton-Schulz runs in place: later calls take the previous result
+        e1.record()
+        torch.cuda.synchronize()
+        ms[k] = e0.elapsed_time(e1) / reps
+    # five steps of A = X X^T, B = b A + c A A, X = a X + B X as dense products
+    dense = sum(5 * (4 * min(R, C) ** 2 * max(R, C) + 2 * min(R, C) ** 3) for R, C in shapes)
+    mfma = muon_tile_flops(shapes)
+    roots_used = len(set(mu.roots))
+    out = {
+        "workload": w.name, "matrices": len(mats), "m_ranks": w.m, "roots_used": roots_used,
+        "real_params": real,
+        "gather": op_entry(ms["gather"], 12 * real),      # g 2, M r/w 8, U 2 per element
+        "apply": op_entry(ms["apply"], 10 * real),        # O 2, theta r/w 8 per element
+        "orthogonalize": {
+            "ms": round(ms["orthogonalize"], 4),
+            "mfma_flops": mfma, "dense_flops": dense,
+            "TFLOP/s": round(mfma / (ms["orthogonalize"] * 1e-3) / 1e12, 1),
+            "frac": round(mfma / (ms["orthogonalize"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "dense_equivalent_TFLOP/s": round(dense / (ms["orthogonalize"] * 1e-3) / 1e12, 1)},
+        "step_ms": round(ms["gather"] + ms["orthogonalize"] + ms["apply"], 4),
+    }
+    mu.free()
+    plan.free()
+    del theta, mom, grad, root
+    torch.cuda.empty_cache()
+    return out
+
+
 # ------------------------------------------------------------ CPU baseline
 
 def _cpu_model() -> str:
@@ -564,6 +651,7 @@ def main():
     }
     if not args.no_per_config:
         result["per_config"] = per_config(dev, max(5, args.steps // 2), 2)
+        result["muon"] = [muon_bench(dev, n, r) for n, r in MUON_CASES]
     if args.cpu_budget > 0 and args.rank is None:
         result["cpu_baseline"] = cpu_baseline(w, args.cpu_budget)
     print(json.dumps(result), flush=True)

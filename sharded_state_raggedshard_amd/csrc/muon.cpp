@@ -168,11 +168,12 @@ rs_status rs_muon_plan(const rs_plan* plan, const int32_t* tensors, int32_t n, r
             mm.gn = ceil_div(N, kChunk);
             for (int64_t e = 0; e < N; e += kChunk)
                 M->chunks.push_back(MuonChunk{e, (int32_t)j, (int32_t)std::min(kChunk, N - e)});
-            const int64_t tcount[4] = {
-                ceil_div(mm.R, kPrepTile) * ceil_div(mm.C, kPrepTile),
-                ceil_div(mm.n, kGemmTile) * ceil_div(mm.n, kGemmTile),
-                ceil_div(mm.n, kGemmTile) * ceil_div(mm.n, kGemmTile),
-                ceil_div(mm.k, kGemmTile) * ceil_div(mm.n, kGemmTile)};
+            // A and B are symmetric: their products compute the tiles on and
+            // above the diagonal only
+            const int64_t tn = ceil_div(mm.n, kGemmTile);
+            const int64_t tcount[4] = {ceil_div(mm.R, kPrepTile) * ceil_div(mm.C, kPrepTile),
+                                       tn * (tn + 1) / 2, tn * (tn + 1) / 2,
+                                       ceil_div(mm.k, kGemmTile) * tn};
             for (int w = 0; w < 4; ++w)
                 M->tiles[size_t(w * (nm + 1) + j + 1)] = M->tiles[size_t(w * (nm + 1) + j)] + tcount[w];
         }

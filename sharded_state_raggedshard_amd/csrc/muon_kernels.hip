@@ -213,8 +213,14 @@ struct GemmArgs {
 // K in steps of 64 through two LDS buffers, the next step's global loads in
 // flight while the current one is multiplied.
 __global__ __launch_bounds__(GT) void ns_gemm_kernel(GemmArgs g) {
-    __shared__ __attribute__((aligned(16))) uint16_t sP[2][BM * LDSR];
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BN * LDSR];
+    // K loop: two buffers of the P and Q tiles; epilogue: the bf16 result
+    // tile, straight and transposed
+    constexpr int kStage = BM * LDSR;
+    constexpr int kOutR = BN + 8;  // bf16 per row of the staged result tiles
+    static_assert(2 * BM * kOutR <= 4 * kStage, "result tiles fit the K-loop buffers");
+    __shared__ __attribute__((aligned(16))) uint16_t lds[4 * kStage];
+    uint16_t(*sP)[kStage] = reinterpret_cast<uint16_t(*)[kStage]>(lds);
+    uint16_t(*sQ)[kStage] = reinterpret_cast<uint16_t(*)[kStage]>(lds + 2 * kStage);
     const int nm = g.t.nm;
     const int64_t* pre = g.t.tiles + (int64_t)(1 + g.kind) * (nm + 1);
     const int64_t tg = pre[g.i0] + blockIdx.x;
@@ -263,8 +269,25 @@ __global__ __launch_bounds__(GT) void ns_gemm_kernel(GemmArgs g) {
         }
     }
     const int64_t ntn = (N + BN - 1) / BN;
-    const int64_t local = tg - pre[mi];
-    const int64_t m0 = (local / ntn) * BM, n0 = (local % ntn) * BN;
+    int64_t local = tg - pre[mi];
+    int64_t tm, tn;
+    if (g.kind == G_UPDATE) {
+        tm = local / ntn;
+        tn = local % ntn;
+    } else {
+        // symmetric result: only tiles tm <= tn, each also stored transposed
+        tm = 0;
+        while (local >= ntn - tm) {
+            local -= ntn - tm;
+            ++tm;
+        }
+        tn = tm + local;
+        if (tn != tm) {
+            Ct = Cs;
+            ldct = ldc;
+        }
+    }
+    const int64_t m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
@@ -326,34 +349,47 @@ __global__ __launch_bounds__(GT) void ns_gemm_kernel(GemmArgs g) {
         b ^= 1;
     }
     // epilogue: lane l holds column l % 32 of a 32 x 32 tile, register r its
-    // row 8 (r / 4) + 4 (l / 32) + r % 4
+    // row 8 (r / 4) + 4 (l / 32) + r % 4.  The bf16 results go to LDS, straight
+    // (sS[row][col]) and transposed (sT[col][row]); then whole rows of both
+    // leave as 16-byte stores.  (The K loop's last barrier has freed LDS.)
+    uint16_t* sS = lds;
+    uint16_t* sT = lds + BM * kOutR;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
-                const int64_t gn = n0 + wn * 64 + j * 32 + (lane & 31);
-                const int64_t gm0 = m0 + wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
+                const int col = wn * 64 + j * 32 + (lane & 31);
+                const int row0 = wm * 64 + i * 32 + 8 * q + 4 * (lane >> 5);
+                const int64_t gn = n0 + col;
                 uint32_t h[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int64_t gm = gm0 + r;
+                    const int64_t gm = m0 + row0 + r;
                     float v = alpha * acc[i][j][4 * q + r];
                     if (Rr && gm < M && gn < N) v = v + beta * bf16_val(Rr[gm * ldr + gn]);
                     h[r] = bf16_bits(v);
-                    if (Cs && gm < M && gn < N) Cs[gm * ldc + gn] = (uint16_t)h[r];
+                    if (Cs) sS[(row0 + r) * kOutR + col] = (uint16_t)h[r];
                 }
-                if (Ct && gn < N) {
-                    if (gm0 + 3 < M) {
-                        *reinterpret_cast<uint2*>(Ct + gn * ldct + gm0) =
-                            make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
-                    } else {
-                        for (int r = 0; r < 4; ++r)
-                            if (gm0 + r < M) Ct[gn * ldct + gm0 + r] = (uint16_t)h[r];
-                    }
-                }
+                if (Ct)
+                    *reinterpret_cast<uint2*>(&sT[col * kOutR + row0]) =
+                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
             }
+    __syncthreads();
+    // M, N and the leading dimensions are multiples of 8: a 16-byte vector is
+    // wholly inside or wholly outside the matrix
+#pragma unroll
+    for (int v = 0; v < (BM * BN / 8) / GT; ++v) {
+        const int idx = v * GT + tid;
+        const int row = idx >> 4, c8 = (idx & 15) * 8;
+        if (Cs && m0 + row < M && n0 + c8 < N)
+            *reinterpret_cast<uint4*>(Cs + (m0 + row) * ldc + n0 + c8) =
+                *reinterpret_cast<const uint4*>(&sS[row * kOutR + c8]);
+        if (Ct && n0 + row < N && m0 + c8 < M)
+            *reinterpret_cast<uint4*>(Ct + (n0 + row) * ldct + m0 + c8) =
+                *reinterpret_cast<const uint4*>(&sT[row * kOutR + c8]);
+    }
 }
 
 // ---------------------------------------------------------------- apply
