@@ -26,7 +26,7 @@ struct rs_muon {
     std::vector<rs::mu::MuonMat> mats;  // sorted by (root, given order)
     std::vector<int32_t> slot_of;       // given index -> index in mats
     std::vector<rs::mu::MuonChunk> chunks;
-    std::vector<int64_t> tiles;         // [prep | gram | poly | update] x (nm + 1) prefix counts
+    std::vector<int64_t> tiles;         // 7 prefix tile tables (see rs::mu::Tables)
     std::vector<int64_t> region;        // m + 1 region starts in the root buffer
     std::vector<int32_t> first;         // m + 1: matrices of root r are [first[r], first[r + 1])
     int64_t root_elems = 0;
@@ -149,7 +149,7 @@ rs_status rs_muon_plan(const rs_plan* plan, const int32_t* tensors, int32_t n, r
         M->root_elems = off;
         // Newton-Schulz buffers, chunks and tile counts
         const int64_t nm = (int64_t)M->mats.size();
-        M->tiles.assign(size_t(4 * (nm + 1)), 0);
+        M->tiles.assign(size_t(7 * (nm + 1)), 0);
         int64_t ns = 0;
         auto take = [&](int64_t elems) {
             const int64_t o = ns;
@@ -170,11 +170,13 @@ rs_status rs_muon_plan(const rs_plan* plan, const int32_t* tensors, int32_t n, r
                 M->chunks.push_back(MuonChunk{e, (int32_t)j, (int32_t)std::min(kChunk, N - e)});
             // A and B are symmetric: their products compute the tiles on and
             // above the diagonal only
-            const int64_t tn = ceil_div(mm.n, kGemmTile);
-            const int64_t tcount[4] = {ceil_div(mm.R, kPrepTile) * ceil_div(mm.C, kPrepTile),
+            const int64_t tn = ceil_div(mm.n, kGemmTile), tn2 = ceil_div(mm.n, kGemmTile2);
+            const int64_t tcount[7] = {ceil_div(mm.R, kPrepTile) * ceil_div(mm.C, kPrepTile),
                                        tn * (tn + 1) / 2, tn * (tn + 1) / 2,
-                                       ceil_div(mm.k, kGemmTile) * tn};
-            for (int w = 0; w < 4; ++w)
+                                       ceil_div(mm.k, kGemmTile) * tn,
+                                       tn2 * (tn2 + 1) / 2, tn2 * (tn2 + 1) / 2,
+                                       ceil_div(mm.k, kGemmTile2) * tn2};
+            for (int w = 0; w < 7; ++w)
                 M->tiles[size_t(w * (nm + 1) + j + 1)] = M->tiles[size_t(w * (nm + 1) + j)] + tcount[w];
         }
         if (M->chunks.size() > 0x7fffffffu) {
@@ -280,8 +282,11 @@ rs_status rs_muon_orthogonalize(const rs_muon* muon, int32_t root, uint16_t* d_r
     int64_t c0, c1;
     rs_status st = select(*muon, root, i0, i1, c0, c1);
     if (st != RS_OK) return st;
+    bool wide = true;
+    for (int32_t i = i0; i < i1; ++i)
+        wide = wide && muon->mats[size_t(i)].n % 32 == 0 && muon->mats[size_t(i)].k % 32 == 0;
     hipError_t e = rs::mu::launch_orthogonalize(device_tables(*muon), muon->tiles.data(), i0, i1,
-                                                c0, c1, d_root,
+                                                c0, c1, wide, d_root,
                                                 reinterpret_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(RS_EHIP, std::string("Newton-Schulz launch: ") + hipGetErrorString(e));

@@ -204,8 +204,93 @@ struct GemmArgs {
     int32_t kind;  // G_GRAM, G_POLY, G_UPDATE
     int32_t it;    // Newton-Schulz step (selects the Y buffers)
     int32_t last;  // last step: the result goes to the root buffer
+    int32_t table; // which prefix tile table (tile size) the launch counts on
     uint16_t* root;
 };
+
+// One product of a Newton-Schulz step: C = alpha P Q^T + beta R, P: M x K and
+// Q: N x K read along rows; R and C: M x N; Rt = R^T (N x M, row-major) for
+// kernels that read the addend by columns; Cs / Ct: where C goes straight /
+// transposed (either may be null).  All bf16, leading dimensions in elements.
+struct Prod {
+    const uint16_t *P, *Q, *Rr, *Rt;
+    uint16_t *Cs, *Ct;
+    int64_t M, N, K, ldp, ldq, ldr, ldrt, ldc, ldct;
+    float alpha, beta;
+};
+
+__device__ __forceinline__ Prod product_of(const GemmArgs& g, const MuonMat& md) {
+    uint16_t* ws = g.t.ws;
+    const int64_t yin = (g.it & 1) ? md.y1 : md.y0;
+    const int64_t yout = (g.it & 1) ? md.y0 : md.y1;
+    Prod p;
+    p.Rr = p.Rt = nullptr;
+    p.Cs = p.Ct = nullptr;
+    p.ldr = p.ldrt = p.ldc = p.ldct = 0;
+    p.alpha = 1.0f;
+    p.beta = 0.0f;
+    if (g.kind == G_GRAM) {  // A = X X^T
+        p.P = p.Q = ws + md.x;
+        p.ldp = p.ldq = md.k;
+        p.M = p.N = md.n;
+        p.K = md.k;
+        p.Cs = ws + md.a;
+        p.ldc = md.n;
+    } else if (g.kind == G_POLY) {  // B = c A A^T + b A  (A = A^T)
+        p.P = p.Q = p.Rr = p.Rt = ws + md.a;
+        p.ldp = p.ldq = p.ldr = p.ldrt = md.n;
+        p.M = p.N = p.K = md.n;
+        p.alpha = kNsC;
+        p.beta = kNsB;
+        p.Cs = ws + md.b;
+        p.ldc = md.n;
+    } else {  // Y' = Y B^T + a Y, stored as Y' and as X' = Y'^T  (Y^T = X)
+        p.P = p.Rr = ws + yin;
+        p.Rt = ws + md.x;
+        p.Q = ws + md.b;
+        p.ldp = p.ldq = p.ldr = md.n;
+        p.ldrt = md.k;
+        p.M = md.k;
+        p.N = p.K = md.n;
+        p.beta = kNsA;
+        if (!g.last) {
+            p.Cs = ws + yout;
+            p.ldc = md.n;
+            p.Ct = ws + md.x;
+            p.ldct = md.k;
+        } else if (md.tr) {  // the result is Y (R x C, C = n)
+            p.Cs = g.root + md.root_off;
+            p.ldc = md.n;
+        } else {  // the result is X (R x C, C = k)
+            p.Ct = g.root + md.root_off;
+            p.ldct = md.k;
+        }
+    }
+    return p;
+}
+
+// Output tile (tm, tn) of the launch's tile `local` of a product: every tile
+// of the update; for the symmetric products only tm <= tn, each tile then
+// also stored transposed into the same matrix (off the diagonal).
+__device__ __forceinline__ void tile_of_product(const GemmArgs& g, Prod& p, int64_t local,
+                                                int64_t tile, int64_t& tm, int64_t& tn) {
+    const int64_t ntn = (p.N + tile - 1) / tile;
+    if (g.kind == G_UPDATE) {
+        tm = local / ntn;
+        tn = local % ntn;
+        return;
+    }
+    tm = 0;
+    while (local >= ntn - tm) {
+        local -= ntn - tm;
+        ++tm;
+    }
+    tn = tm + local;
+    if (tn != tm) {
+        p.Ct = p.Cs;
+        p.ldct = p.ldc;
+    }
+}
 
 // One 128 x 128 tile of C = alpha P Q^T + beta R (P: M x K, Q: N x K, R and
 // C: M x N, all row-major bf16), stored straight (Cs) and/or transposed
@@ -222,71 +307,17 @@ __global__ __launch_bounds__(GT) void ns_gemm_kernel(GemmArgs g) {
     uint16_t(*sP)[kStage] = reinterpret_cast<uint16_t(*)[kStage]>(lds);
     uint16_t(*sQ)[kStage] = reinterpret_cast<uint16_t(*)[kStage]>(lds + 2 * kStage);
     const int nm = g.t.nm;
-    const int64_t* pre = g.t.tiles + (int64_t)(1 + g.kind) * (nm + 1);
+    const int64_t* pre = g.t.tiles + (int64_t)g.table * (nm + 1);
     const int64_t tg = pre[g.i0] + blockIdx.x;
     const int mi = find_mat(pre, g.i0, g.i1, tg);
-    const MuonMat& md = g.t.mats[mi];
-    uint16_t* ws = g.t.ws;
-    const int64_t yin = (g.it & 1) ? md.y1 : md.y0;
-    const int64_t yout = (g.it & 1) ? md.y0 : md.y1;
-    const uint16_t *P, *Q, *Rr = nullptr;
-    uint16_t *Cs = nullptr, *Ct = nullptr;
-    int64_t M, N, K, ldp, ldq, ldr = 0, ldc = 0, ldct = 0;
-    float alpha = 1.0f, beta = 0.0f;
-    if (g.kind == G_GRAM) {  // A = X X^T
-        P = Q = ws + md.x;
-        ldp = ldq = md.k;
-        M = N = md.n;
-        K = md.k;
-        Cs = ws + md.a;
-        ldc = md.n;
-    } else if (g.kind == G_POLY) {  // B = c A A^T + b A
-        P = Q = Rr = ws + md.a;
-        ldp = ldq = ldr = md.n;
-        M = N = K = md.n;
-        alpha = kNsC;
-        beta = kNsB;
-        Cs = ws + md.b;
-        ldc = md.n;
-    } else {  // Y' = Y B^T + a Y, stored as Y' and as X' = Y'^T
-        P = Rr = ws + yin;
-        Q = ws + md.b;
-        ldp = ldq = ldr = md.n;
-        M = md.k;
-        N = K = md.n;
-        beta = kNsA;
-        if (!g.last) {
-            Cs = ws + yout;
-            ldc = md.n;
-            Ct = ws + md.x;
-            ldct = md.k;
-        } else if (md.tr) {  // the result is Y (R x C, C = n)
-            Cs = g.root + md.root_off;
-            ldc = md.n;
-        } else {  // the result is X (R x C, C = k)
-            Ct = g.root + md.root_off;
-            ldct = md.k;
-        }
-    }
-    const int64_t ntn = (N + BN - 1) / BN;
-    int64_t local = tg - pre[mi];
+    Prod pr = product_of(g, g.t.mats[mi]);
     int64_t tm, tn;
-    if (g.kind == G_UPDATE) {
-        tm = local / ntn;
-        tn = local % ntn;
-    } else {
-        // symmetric result: only tiles tm <= tn, each also stored transposed
-        tm = 0;
-        while (local >= ntn - tm) {
-            local -= ntn - tm;
-            ++tm;
-        }
-        tn = tm + local;
-        if (tn != tm) {
-            Ct = Cs;
-            ldct = ldc;
-        }
-    }
+    tile_of_product(g, pr, tg - pre[mi], BM, tm, tn);
+    const uint16_t *P = pr.P, *Q = pr.Q, *Rr = pr.Rr;
+    uint16_t *Cs = pr.Cs, *Ct = pr.Ct;
+    const int64_t M = pr.M, N = pr.N, K = pr.K, ldp = pr.ldp, ldq = pr.ldq, ldr = pr.ldr,
+                  ldc = pr.ldc, ldct = pr.ldct;
+    const float alpha = pr.alpha, beta = pr.beta;
     const int64_t m0 = tm * BM, n0 = tn * BN;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -392,6 +423,188 @@ __global__ __launch_bounds__(GT) void ns_gemm_kernel(GemmArgs g) {
     }
 }
 
+// ------------------------------------------------ 256 x 256 products
+
+constexpr int T2 = 256, BK2 = 32, NSTAGE = 4;
+constexpr int kStage2 = T2 * BK2;      // bf16 of one operand tile in LDS (16 KiB)
+constexpr int kOutR2 = T2 + 8;         // bf16 per row of the staged result tile
+static_assert(T2 * kOutR2 >= 2 * NSTAGE * kStage2, "the staged result tile covers the stages");
+
+// s_waitcnt immediate (gfx9 encoding) that waits until at most n vector
+// memory operations of the wave are outstanding, leaving the other counters.
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// A T2 x 32 bf16 tile (rows r0 .., k0 .. k0 + 31 of a row-major matrix) into
+// LDS, straight from global memory (gfx950's 16-byte loads to LDS, no VGPR
+// staging).  LDS rows are 64 bytes; the 16-byte chunk c of row r sits at
+// chunk c ^ ((r >> 2) & 3), so the 16 lanes of a fragment read meet 16
+// different bank groups.  Wave w fills rows [64 w, 64 w + 64), sixteen rows
+// per instruction (lane l: row l / 4, physical chunk l % 4).  Rows past rmax
+// read row rmax - 1: they only feed results outside the matrix, which are
+// never stored.
+__device__ __forceinline__ void tile_to_lds(const uint16_t* A, int64_t ld, int64_t r0,
+                                            int64_t rmax, int64_t k0, uint16_t* dst) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int row = wave * 64 + j * 16 + (lane >> 2);
+        const int lc = (lane & 3) ^ ((row >> 2) & 3);
+        int64_t gr = r0 + row;
+        gr = gr < rmax ? gr : rmax - 1;
+        __builtin_amdgcn_global_load_lds(A + gr * ld + k0 + lc * 8,
+                                         dst + (wave * 64 + j * 16) * BK2, 16, 0, 0);
+    }
+}
+
+__device__ __forceinline__ bf16x8 frag2(const uint16_t* src, int row, int lc) {
+    return *reinterpret_cast<const bf16x8*>(src + row * BK2 + ((lc ^ ((row >> 2) & 3)) << 3));
+}
+
+// One 256 x 256 tile of a product whose K is a multiple of 32.  Four waves,
+// each a 128 x 128 quarter as 4 x 4 MFMA tiles (256 accumulators per lane);
+// both operand tiles go straight to LDS through four stages, loads issued
+// three stages ahead of the multiplications so that their latency is hidden
+// behind three stages of MFMA work.  The addend is read through its
+// transpose Rt (A itself, or X for Y), so the four consecutive rows a lane
+// holds for one column are 8 contiguous bytes.  One workgroup per compute
+// unit (132 KiB of LDS).
+__global__ __launch_bounds__(GT) void ns_gemm256_kernel(GemmArgs g) {
+    __shared__ __attribute__((aligned(16))) uint16_t lds[T2 * kOutR2];
+    const int nm = g.t.nm;
+    const int64_t* pre = g.t.tiles + (int64_t)g.table * (nm + 1);
+    const int64_t tg = pre[g.i0] + blockIdx.x;
+    const int mi = find_mat(pre, g.i0, g.i1, tg);
+    Prod p = product_of(g, g.t.mats[mi]);
+    int64_t tm, tn;
+    tile_of_product(g, p, tg - pre[mi], T2, tm, tn);
+    const int64_t m0 = tm * T2, n0 = tn * T2;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+
+    const int frow = lane & 31, half = lane >> 5;
+    // lane l holds column l % 32 of each 32 x 32 MFMA tile, register r its
+    // row 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive rows per register
+    // group
+    auto row_of = [&](int i, int q) { return wm * 128 + i * 32 + 8 * q + 4 * half; };
+    auto col_of = [&](int j) { return wn * 128 + j * 32 + frow; };
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+    const int KT = (int)(p.K / BK2);
+    auto issue = [&](int kt) {
+        uint16_t* st = lds + (kt % NSTAGE) * 2 * kStage2;
+        tile_to_lds(p.P, p.ldp, m0, p.M, (int64_t)kt * BK2, st);
+        tile_to_lds(p.Q, p.ldq, n0, p.N, (int64_t)kt * BK2, st + kStage2);
+    };
+    for (int s = 0; s < NSTAGE - 1; ++s)
+        if (s < KT) issue(s);
+    for (int kt = 0; kt < KT; ++kt) {
+        // stage kt has landed once at most the later stages' loads (8 per
+        // stage per wave) are outstanding; the barrier then also tells every
+        // wave that all are done reading the stage the next issue overwrites
+        const int later = min(NSTAGE - 2, KT - 1 - kt);
+        if (later >= 2)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+        else if (later == 1)
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+        else
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+        // a bare barrier (also a compiler memory fence): __syncthreads would
+        // first wait for every outstanding load, the stages still in flight
+        // included
+        asm volatile("s_barrier" ::: "memory");
+        if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
+        const uint16_t* sp = lds + (kt % NSTAGE) * 2 * kStage2;
+        const uint16_t* sq = sp + kStage2;
+        // every fragment of the stage is read up front (16 reads), then the 32
+        // MFMAs run back to back
+        bf16x8 fa[BK2 / 16][4], fb[BK2 / 16][4];
+#pragma unroll
+        for (int kk = 0; kk < BK2 / 16; ++kk) {
+            const int lc = 2 * kk + half;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) fa[kk][i] = frag2(sp, wm * 128 + i * 32 + frow, lc);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) fb[kk][j] = frag2(sq, wn * 128 + j * 32 + frow, lc);
+        }
+#pragma unroll
+        for (int kk = 0; kk < BK2 / 16; ++kk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j],
+                                                                        acc[i][j], 0, 0, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+    }
+    __syncthreads();  // every wave is done with the stages: LDS is free
+    // results alpha acc + beta R, straight then transposed, each staged
+    // through LDS and stored as 16-byte row pieces (M, N and the leading
+    // dimensions are multiples of 8)
+    uint16_t* so = lds;
+    // addend of 32 x 32 tile (i, j), register group q: 8 bytes of Rt
+    auto load_r = [&](int i, int j, uint2 (&w)[4]) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int row = row_of(i, q), col = col_of(j);
+            w[q] = make_uint2(0u, 0u);
+            if (p.Rt && m0 + row < p.M && n0 + col < p.N)
+                w[q] = *reinterpret_cast<const uint2*>(p.Rt + (n0 + col) * p.ldrt + m0 + row);
+        }
+    };
+    for (int pass = 0; pass < 2; ++pass) {
+        uint16_t* out = pass == 0 ? p.Cs : p.Ct;
+        if (!out) continue;
+        // the addend of the next 32 x 32 tile is in flight while this one is
+        // formed (one tile's loads at a time: the scheduler barrier keeps the
+        // compiler from hoisting all 64 of them)
+        uint2 rcur[4], rnxt[4];
+        load_r(0, 0, rcur);
+#pragma unroll
+        for (int ij = 0; ij < 16; ++ij) {
+            const int i = ij >> 2, j = ij & 3;
+            if (ij + 1 < 16) load_r((ij + 1) >> 2, (ij + 1) & 3, rnxt);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int row = row_of(i, q), col = col_of(j);
+                const float rv[4] = {bf16_val(rcur[q].x & 0xffffu), bf16_val(rcur[q].x >> 16),
+                                     bf16_val(rcur[q].y & 0xffffu), bf16_val(rcur[q].y >> 16)};
+                uint32_t h[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h[r] = bf16_bits(p.alpha * acc[i][j][4 * q + r] + p.beta * rv[r]);
+                if (pass == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) so[(row + r) * kOutR2 + col] = (uint16_t)h[r];
+                } else {
+                    *reinterpret_cast<uint2*>(so + col * kOutR2 + row) =
+                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) rcur[q] = rnxt[q];
+        }
+        __syncthreads();
+        const int64_t ra = pass == 0 ? m0 : n0, ca = pass == 0 ? n0 : m0;
+        const int64_t rlim = pass == 0 ? p.M : p.N, clim = pass == 0 ? p.N : p.M;
+        const int64_t ld = pass == 0 ? p.ldc : p.ldct;
+        for (int v = tid; v < T2 * (T2 / 8); v += GT) {
+            const int rr = v / (T2 / 8), c8 = (v % (T2 / 8)) * 8;
+            if (ra + rr < rlim && ca + c8 < clim)
+                *reinterpret_cast<uint4*>(out + (ra + rr) * ld + ca + c8) =
+                    *reinterpret_cast<const uint4*>(so + rr * kOutR2 + c8);
+        }
+        __syncthreads();
+    }
+}
+
 // ---------------------------------------------------------------- apply
 
 __global__ __launch_bounds__(kVT) void apply_kernel(Tables t, int64_t c0, float* __restrict__ theta,
@@ -432,7 +645,7 @@ hipError_t launch_gather(const Tables& t, int64_t c0, int64_t c1, float* mom, co
 }
 
 hipError_t launch_orthogonalize(const Tables& t, const int64_t* host_tiles, int32_t i0, int32_t i1,
-                                int64_t c0, int64_t c1, uint16_t* root, hipStream_t s) {
+                                int64_t c0, int64_t c1, bool wide, uint16_t* root, hipStream_t s) {
     if (i1 <= i0) return hipSuccess;
     const int64_t stride = t.nm + 1;
     auto count = [&](int which) {
@@ -454,7 +667,15 @@ hipError_t launch_orthogonalize(const Tables& t, const int64_t* host_tiles, int3
             a.it = it;
             a.last = it == kNsSteps - 1;
             a.root = root;
-            hipLaunchKernelGGL(ns_gemm_kernel, dim3((unsigned)count(1 + kind)), dim3(GT), 0, s, a);
+            if (wide) {
+                a.table = 4 + kind;
+                hipLaunchKernelGGL(ns_gemm256_kernel, dim3((unsigned)count(4 + kind)), dim3(GT), 0,
+                                   s, a);
+            } else {
+                a.table = 1 + kind;
+                hipLaunchKernelGGL(ns_gemm_kernel, dim3((unsigned)count(1 + kind)), dim3(GT), 0,
+                                   s, a);
+            }
             e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
