@@ -85,6 +85,8 @@ def lib():
         L.orc_bruteforce_feasible_at.argtypes = [C.POINTER(_Tensor), C.c_int, C.c_int,
                                                  C.c_int64, C.c_int64, P64]
         L.orc_wide_tensor_ok.argtypes = [C.POINTER(_Tensor), C.c_int, C.c_int64, C.c_int64]
+        L.orc_count_cut_blocks.argtypes = [C.POINTER(_Tensor), C.c_int, C.c_int64, P64]
+        L.orc_count_cut_blocks.restype = C.c_int64
         L.orc_bf16.argtypes = [C.c_float]
         L.orc_bf16.restype = C.c_uint16
         L.orc_bf16_to_f32.argtypes = [C.c_uint16]
@@ -254,6 +256,17 @@ def check_plan(specs: Sequence, m: int, g_coll: int, S: int, offsets: Sequence[i
     n = len(specs)
     off = (C.c_int64 * n)(*offsets)
     return int(lib().orc_check_plan(_tensors(specs, align_unit), n, m, g_coll, S, off))
+
+
+def count_cut_blocks(specs: Sequence, S: int, offsets: Sequence[int]) -> int:
+    """Blocks with elements in two ranks of size S, tensor i at offsets[i]
+    (any offsets; the count invariant I1 requires to be zero)."""
+    n = len(specs)
+    off = (C.c_int64 * n)(*offsets)
+    r = int(lib().orc_count_cut_blocks(_tensors(specs), n, S, off))
+    if r < 0:
+        raise ValueError("invalid input")
+    return r
 
 
 def block_first_position(spec, p0: int, k: int) -> int:

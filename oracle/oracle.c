@@ -286,6 +286,22 @@ static void block_extent(const orc_tensor* t, const orc_derived* d, int64_t p0, 
     }
 }
 
+int64_t orc_count_cut_blocks(const orc_tensor* ts, int n, int64_t S, const int64_t* off) {
+    if (!ts || !off || n < 0 || S <= 0) return -1;
+    int64_t cut = 0;
+    for (int t = 0; t < n; ++t) {
+        orc_derived d;
+        if (orc_derive(&ts[t], 1, &d)) return -1;
+        if (ts[t].gran == ORC_ELEMENT) continue;
+        for (int64_t k = 0; k < d.nblk; ++k) {
+            int64_t lo, hi;
+            block_extent(&ts[t], &d, off[t], k, &lo, &hi);
+            if (lo / S != hi / S) ++cut;
+        }
+    }
+    return cut;
+}
+
 int orc_check_plan(const orc_tensor* ts, int n, int m, int64_t g_coll, int64_t S,
                    const int64_t* off) {
     orc_derived* d = (orc_derived*)calloc((size_t)n, sizeof(orc_derived));

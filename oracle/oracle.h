@@ -94,6 +94,12 @@ int orc_bruteforce_feasible_at(const orc_tensor* ts, int n, int m, int64_t g_col
  * input. */
 int orc_wide_tensor_ok(const orc_tensor* ts, int n, int64_t g_coll, int64_t S);
 
+/* Blocks with elements in two ranks (rank = position / S) when tensor t
+ * starts at off[t]; offsets are taken as given (no order, alignment or
+ * bound is checked), so naive layouts can be counted too.  Invariant I1 of
+ * a plan is this count being zero.  -1 on invalid input. */
+int64_t orc_count_cut_blocks(const orc_tensor* ts, int n, int64_t S, const int64_t* off);
+
 /* Invariants I1..I5 of a bucket plan.  Returns 0 if all hold, otherwise the
  * number (1..5) of the first violated invariant. */
 int orc_check_plan(const orc_tensor* ts, int n, int m, int64_t g_coll, int64_t S,

@@ -22,7 +22,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 
 COMMON = [
-    "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
+    "-O3", "-std=c++17", "-fPIC", "-pthread", "-Wall", "-Wno-unused-function",
     f"--offload-arch={ARCH}",
     # binary32 semantics the step relies on: no FMA contraction, correctly
     # rounded '/' and sqrt
@@ -51,7 +51,7 @@ def build(verbose: bool = False) -> str:
     with cf.ThreadPoolExecutor(max_workers=min(4, len(SOURCES))) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = OUT + ".tmp"
-    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-pthread", "-o", tmp, *objs,
            "-Wl,-rpath,/opt/rocm/lib"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:

@@ -11,18 +11,24 @@
 // previous tensor ends, and an earlier end never removes an admissible
 // offset, so earliest-offset placement is exact for that S (the page's
 // monotone dp(t, i) for a fixed order).  Feasibility is not monotone in S,
-// so S is scanned upward; two devices keep the scan short:
-//   - a tensor longer than 2S always holds two consecutive rank boundaries,
-//     so S must be a multiple of its cut unit: the scan jumps to the next
-//     such S until a tensor stops being that long;
+// so S is scanned upward; three devices keep the scan short:
+//   - each long tensor rules out values of S by itself (SFilter below), and
+//     the scan jumps over them;
 //   - inside one S, the earliest offset jumps straight to the next offset
 //     that repairs the first offending boundary (Chinese remaindering of the
-//     alignment and the cut unit) instead of stepping by the alignment.
+//     alignment and the cut unit) instead of stepping by the alignment;
+//   - a scan that is still going after a few thousand values of S continues
+//     on several host threads, each taking the next range of S in
+//     increasing order; the smallest feasible S is the same whatever the
+//     threads' timing.
 #include "plan.hpp"
 
 #include <algorithm>
-#include <map>
+#include <atomic>
 #include <limits>
+#include <map>
+#include <system_error>
+#include <thread>
 
 namespace rs {
 
@@ -205,6 +211,70 @@ bool place_all(const std::vector<TensorInfo*>& ts, const std::vector<int64_t>& r
     return true;
 }
 
+// What one tensor alone says about S.  A tensor longer than S holds a rank
+// boundary j S (0 < j < m) strictly inside it, which must lie on a cut:
+// j S = o (mod u) for its offset o, a multiple of A, so j S is a multiple of
+// h = gcd(A, u), and some j < m achieves that only when h / gcd(S, h) <=
+// m - 1.  A tensor longer than 2S holds two consecutive boundaries, so u
+// divides S.  Both are necessary conditions, so skipping the values of S
+// they exclude never skips a feasible S.
+struct SFilter {
+    int64_t N;
+    int64_t g;                   // S stays a multiple of g_coll
+    int64_t su;                  // lcm(u, g)
+    int64_t h;
+    std::vector<int64_t> steps;  // lcm(h / d, g) for the divisors d <= m - 1 of h
+
+    SFilter(const TensorInfo& t, int32_t m, int64_t g_) : N(t.N), g(g_) {
+        su = lcm_sat(t.u, g);
+        h = gcd64(t.A, t.u);
+        for (int64_t d = 1; d <= std::min<int64_t>(m - 1, h); ++d)
+            if (h % d == 0) steps.push_back(lcm_sat(h / d, g));
+        // keep the steps no other step divides (their multiples cover the rest)
+        std::sort(steps.begin(), steps.end());
+        steps.erase(std::unique(steps.begin(), steps.end()), steps.end());
+        if (steps.size() <= 512) {
+            std::vector<int64_t> keep;
+            for (int64_t st : steps) {
+                bool covered = false;
+                for (int64_t k : keep) covered = covered || st % k == 0;
+                if (!covered) keep.push_back(st);
+            }
+            steps.swap(keep);
+        }
+    }
+
+    // smallest S' >= S (a multiple of g) this tensor does not rule out
+    int64_t next(int64_t S, int32_t m) const {
+        if (N > 2 * S) {
+            if (S % su == 0) return S;
+            return std::min(su >= kInf ? kInf : round_up(S, su), round_up(ceil_div(N, 2), g));
+        }
+        if (N > S && h / gcd64(S, h) > m - 1) {
+            int64_t nxt = round_up(N, g);  // from S >= N on, no boundary has to fall inside
+            for (int64_t st : steps) nxt = std::min(nxt, st >= kInf ? kInf : round_up(S, st));
+            return nxt;
+        }
+        return S;
+    }
+};
+
+// Smallest S' >= S passing every tensor's filter.
+int64_t next_candidate(const std::vector<SFilter>& fs, int32_t m, int64_t S) {
+    for (;;) {
+        int64_t nxt = S;
+        for (const SFilter& f : fs) nxt = std::max(nxt, f.next(S, m));
+        if (nxt == S || nxt >= kInf) return nxt;
+        S = nxt;
+    }
+}
+
+// Candidates tried on the calling thread before the scan goes parallel, and
+// the width (in values of S) of one range of the parallel scan.
+constexpr int kSerialTries = 4096;
+constexpr int64_t kRangeTries = 2048;
+constexpr unsigned kMaxPlanThreads = 16;
+
 rs_status plan_one_bucket(std::vector<TensorInfo*>& ts, int32_t m, int64_t g, int64_t& S_out,
                           std::string& err) {
     int64_t end0 = 0;
@@ -215,29 +285,56 @@ rs_status plan_one_bucket(std::vector<TensorInfo*>& ts, int32_t m, int64_t g, in
     const int64_t S_hi = round_up(end0, g);  // everything inside rank 0: always feasible
     std::vector<int64_t> off(ts.size()), rest(ts.size() + 1, 0);
     for (size_t i = ts.size(); i-- > 0;) rest[i] = rest[i + 1] + ts[i]->N;
+    std::vector<SFilter> fs;
+    for (auto* t : ts)
+        if (t->N > S_lo) fs.emplace_back(*t, m, g);  // S >= S_lo: shorter tensors never filter
+
+    auto done = [&](int64_t S) {
+        place_all(ts, rest, m, S, off);
+        for (size_t i = 0; i < ts.size(); ++i) ts[i]->off = off[i];
+        S_out = S;
+        return RS_OK;
+    };
     int64_t S = S_lo;
-    while (S <= S_hi) {
-        int64_t L = g;
-        int64_t change = kInf;
-        for (auto* t : ts) {
-            if (t->N > 2 * S) {
-                L = lcm_sat(L, t->u);
-                change = std::min(change, ceil_div(t->N, 2));
-            }
-        }
-        if (S % L != 0) {
-            int64_t nxt = (L >= kInf) ? kInf : round_up(S, L);
-            if (change < kInf) nxt = std::min(nxt, round_up(change, g));
-            if (nxt <= S) nxt = S + g;
-            S = nxt;
-            continue;
-        }
-        if (place_all(ts, rest, m, S, off)) {
-            for (size_t i = 0; i < ts.size(); ++i) ts[i]->off = off[i];
-            S_out = S;
-            return RS_OK;
-        }
+    for (int tries = 0; tries < kSerialTries; ++tries) {
+        S = next_candidate(fs, m, S);
+        if (S > S_hi) break;
+        if (place_all(ts, rest, m, S, off)) return done(S);
         S += g;
+    }
+    if (S <= S_hi) {
+        // the rest of [S, S_hi] in ranges handed out in increasing order; a
+        // range starting past the best S found so far is not needed
+        const int64_t width = kRangeTries * g;
+        std::atomic<int64_t> next_start{S}, best{kInf};
+        auto worker = [&]() {
+            std::vector<int64_t> o(ts.size());
+            for (;;) {
+                const int64_t a = next_start.fetch_add(width);
+                if (a > S_hi || a >= best.load()) return;
+                const int64_t b = std::min(a + width, S_hi + 1);
+                for (int64_t s = next_candidate(fs, m, a); s < b && s < best.load();
+                     s = next_candidate(fs, m, s + g)) {
+                    if (place_all(ts, rest, m, s, o)) {
+                        int64_t cur = best.load();
+                        while (s < cur && !best.compare_exchange_weak(cur, s)) {
+                        }
+                        break;
+                    }
+                }
+            }
+        };
+        unsigned nt = std::thread::hardware_concurrency();
+        nt = std::max(1u, std::min(nt, kMaxPlanThreads));
+        std::vector<std::thread> pool;
+        try {
+            for (unsigned i = 1; i < nt; ++i) pool.emplace_back(worker);
+        } catch (const std::system_error&) {
+            // fewer threads than asked for: the ones running (and this one) finish the scan
+        }
+        worker();
+        for (auto& th : pool) th.join();
+        if (best.load() < kInf) return done(best.load());
     }
     err = "internal: planner scan ended without a placement";
     return RS_EINVAL;

@@ -130,6 +130,52 @@ def test_product_planner_matches_oracle_on_workloads(name):
     rs.rs_plan_free(h)
 
 
+def test_product_planner_matches_oracle_with_tensors_longer_than_S():
+    # a few long row-block tensors and few ranks: tensors longer than S (one
+    # rank boundary inside) and longer than 2S (two) decide which S the
+    # product's scan may skip; the oracle tries every S
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        specs = []
+        for i in range(int(rng.integers(1, 5))):
+            C_ = int(rng.choice([1, 4, 12, 16, 24]))
+            R = int(rng.integers(8, 400))
+            specs.append(TensorSpec(f"r{i}", (R, C_), ROWS, int(rng.integers(1, 24))))
+        if rng.integers(0, 2):
+            specs.insert(int(rng.integers(0, len(specs) + 1)),
+                         TensorSpec("e", (int(rng.integers(1, 200)),), ELEMENT))
+        m = int(rng.integers(2, 10))
+        g = int(rng.choice([1, 2, 16]))
+        h, L = _compare_plan(specs, m, g)
+        rs.rs_plan_free(h)
+
+
+@pytest.mark.parametrize("bucket,m", [(1, 8), (4, 16)])
+def test_product_planner_matches_oracle_on_long_scans(bucket, m):
+    # DeepSeek-V3-shaped layer buckets at 128-row blocks: the dense layer at
+    # m = 8 (the oracle scans about 10^6 values of S, the product skips the
+    # ones its long tensors rule out) and the MoE layer at m = 16 (about
+    # 10^5 values; the product finishes the scan on several threads)
+    specs = [TensorSpec(s.name, s.shape, s.gran, s.br, s.bc, 0)
+             for s in synth.MODEL_SHAPES["deepseek_v3"](128) if s.bucket == bucket]
+    h, L = _compare_plan(specs, m, 16)
+    rs.rs_plan_free(h)
+
+
+@pytest.mark.parametrize("model", ["gpt_oss_120b", "deepseek_v3"])
+def test_planning_time_on_model_inventories(model):
+    # the page reports planning as a one-time cost under 0.3 s; every
+    # granularity and group size of the planning-quality report stays below
+    for rows in (1, 16, 128):
+        specs = synth.MODEL_SHAPES[model](rows)
+        for m in (8, 16, 32, 64, 128, 256):
+            t0 = time.perf_counter()
+            h = rs.rs_plan_layout(specs, m, 16)
+            dt = time.perf_counter() - t0
+            rs.rs_plan_free(h)
+            assert dt < 0.3, (model, rows, m, dt)
+
+
 def test_padding_reported_for_fused_experts():
     # 48 ranks do not divide the 2160 row blocks of the fused experts:
     # S rounds up to 46 blocks of 128 x 2880 and the last rank stays empty.
