@@ -136,7 +136,8 @@ typedef struct {
  * among placements with that S_b the lexicographically smallest offsets.
  * Tensors are placed in the order `order` selects (RS_ORDER_GIVEN: as
  * given); offsets are reported per tensor in the caller's order either way.
- * Host only, synchronous.
+ * Host only, synchronous; a long scan over S runs on up to 16 host threads
+ * (joined before the call returns; the result does not depend on them).
  * On success *out receives a new plan (free with rs_plan_free).
  * Errors: RS_EINVAL (n < 1, m < 1, g_coll < 1, bad spec, empty bucket,
  * unknown order or option bits),
