@@ -320,11 +320,11 @@ __device__ __forceinline__ void vec_params(const ChunkDesc& d, const StepArgs& a
     }
 }
 
-// Back: waits for the block's other chunks if needed (every wave polls the
-// slots itself, no barrier), then quantises and stores codes and absmax.
-template <int KG>
+// Back: waits for the block's other chunks if needed (wave 0 polls, the
+// others wait at a barrier), then quantises and stores codes and absmax.
+template <int NT, int KG>
 __device__ __forceinline__ void vec_back(const ChunkDesc& d, int64_t c, const StepArgs& a,
-                                         VecState<KG>& st) {
+                                         VecState<KG>& st, float* red) {
     constexpr int WSPAN = 256 * KG;
     const StepBuffers& B = a.b;
     const int lane = threadIdx.x & 63;
@@ -336,7 +336,8 @@ __device__ __forceinline__ void vec_back(const ChunkDesc& d, int64_t c, const St
     uint8_t* qv_b = B.qv + d.pos;
     if (st.wait) {
         float x, y;
-        coop_wait(B.coop, B.counters, c - d.part, d.nparts, st.seq, x, y);
+        // red[0..1] are free again after the workgroup max
+        coop_wait_wg<NT>(B.coop, B.counters, c - d.part, d.nparts, st.seq, red, x, y);
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             st.am[k] = x;
@@ -401,7 +402,7 @@ __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const
     VecState<KG> st;
     if (!vec_front<MODE, NT, KG>(d, c, a, s, dqm, dqv, red, in, st)) return;
     if (MODE != MODE_PARTIAL) vec_params<KG>(d, a, in, st);
-    vec_back<KG>(d, c, a, st);
+    vec_back<NT, KG>(d, c, a, st, red);
 }
 
 // --------------------------------------------------- generic block paths

@@ -225,7 +225,8 @@ __device__ __forceinline__ void fp8_pack_chunk(const Fp8Args& a, int64_t c, cons
             }
             const uint32_t seq = *seq_lds;  // written before wg_max2's barriers
             if (threadIdx.x == 0) coop_publish(a.b.coop, c, seq, x, 0.0f);
-            coop_wait(a.b.coop, a.b.counters, c - d.part, d.nparts, seq, x, dummy);
+            // red[0..1] are free again after the workgroup max
+            coop_wait_wg<NT>(a.b.coop, a.b.counters, c - d.part, d.nparts, seq, red, x, dummy);
         }
     }
     const float s = x / 448.0f, y = quant_recip(s);

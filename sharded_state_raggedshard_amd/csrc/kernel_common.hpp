@@ -96,12 +96,15 @@ __device__ __forceinline__ int64_t chunk_of(const Ranges& r, int64_t wg) {
 // chunk publishes its maxima with two relaxed device-scope 64-bit stores,
 // each carrying the sequence number of this call next to the value, so a
 // reader that sees the new sequence also sees that chunk's value and no
-// ordering between the two stores or against other memory is needed.
-// Device-scope atomics bypass the per-XCD L2, so every XCD sees the same
-// words.  A waiting wave polls the slots of all chunks of its block with
-// relaxed loads, one chunk per lane, until all show the sequence, and
-// reduces their maxima.  Two values travel per chunk (the step's m and v
-// maxima; a single-value user publishes 0 as the second).
+// ordering between the two stores or against other memory is needed (an
+// acquire or release fence at device scope would write back or invalidate
+// the XCD's whole L2).  Device-scope atomics bypass the per-XCD L2, so every
+// XCD sees the same words.  One wave of a waiting workgroup polls the slots
+// of all chunks of its block with relaxed loads, one chunk per lane, until
+// all show the sequence, and reduces their maxima; the other waves wait at a
+// barrier, so the polls stay a small share of the memory traffic.  Two
+// values travel per chunk (the step's m and v maxima; a single-value user
+// publishes 0 as the second).
 
 __device__ __forceinline__ uint32_t coop_seq(const PartSlot* slots, int64_t c) {
     const uint64_t w = __hip_atomic_load(&slots[c].m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -156,6 +159,28 @@ __device__ __forceinline__ void coop_wait(const PartSlot* slots, CoopCounters* c
             return;
         }
     }
+}
+
+// The whole workgroup's side of a wait: wave 0 polls, the maxima reach the
+// other waves through LDS (bcast: two floats no other code uses meanwhile).
+template <int NT>
+__device__ __forceinline__ void coop_wait_wg(const PartSlot* slots, CoopCounters* counters,
+                                             int64_t c0, int nparts, uint32_t seq, float* bcast,
+                                             float& am, float& av) {
+    if (NT == 64) {
+        coop_wait(slots, counters, c0, nparts, seq, am, av);
+        return;
+    }
+    if (threadIdx.x < 64) {
+        coop_wait(slots, counters, c0, nparts, seq, am, av);
+        if (threadIdx.x == 0) {
+            bcast[0] = am;
+            bcast[1] = av;
+        }
+    }
+    __syncthreads();
+    am = bcast[0];
+    av = bcast[1];
 }
 
 // Lane element offsets of a vector chunk relative to d.pos: slice k of this
