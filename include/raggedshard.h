@@ -262,7 +262,10 @@ rs_status rs_group_scale(const rs_plan* plan, int32_t bucket, int32_t rank, void
 /* *d_sumsq = sum of float(x)^2 over the selection, squares and sum in
  * binary64 (the global L2 norm is its square root; per-rank values are the
  * partial sums an all-reduce would add).  Deterministic: a fixed two-level
- * reduction order.  NaN / Inf propagate.  d_sumsq: one device double. */
+ * reduction order (per-workgroup sums, then those sums in workgroup order,
+ * added by the grid's last workgroup; one launch).  NaN / Inf propagate.
+ * d_sumsq: one device double.  Uses the plan's workspace: calls on one plan
+ * that overlap (several streams) race (the result may then be NaN). */
 rs_status rs_group_l2norm(const rs_plan* plan, int32_t bucket, int32_t rank, const void* d_buf,
                           int32_t dtype, double* d_sumsq, void* stream);
 
@@ -270,12 +273,15 @@ rs_status rs_group_l2norm(const rs_plan* plan, int32_t bucket, int32_t rank, con
  * capture, allocation-free serving or training loops, harnesses that forbid
  * hipMalloc -- and so may not have uploaded the plan: rs_group_l2norm with
  * the same arguments and result (the same kernels, bit for bit), but its
- * partial sums live in the library's own device array of 2048 binary64
- * values (16 KiB per GPU, held until the process ends) instead of the plan's
- * workspace.  Allocates nothing and needs no rs_plan_upload.  The array
- * holds one partial per first-pass workgroup, and the first pass never uses
- * more than 2048 workgroups; a launch that would need more is rejected with
- * RS_EINVAL.  Every call on one GPU shares the array: calls that overlap on
+ * partial sums live in the library's own device array (2048 partial sums
+ * as tagged 64-bit word pairs and a call counter, 32.25 KiB per GPU, held
+ * until the process ends) instead of the plan's workspace.  Allocates
+ * nothing and needs no rs_plan_upload.  The array holds one partial per
+ * workgroup, and the launch never uses more than 2048 workgroups; a launch
+ * that would need more is rejected with RS_EINVAL.  Each call tags its
+ * partials with the next value of the counter (zero when the library
+ * loads), so what earlier calls left in the array is never taken and
+ * nothing needs clearing between calls.  Every call on one GPU shares the array: calls that overlap on
  * one GPU (several streams, several threads) race and must be ordered by the
  * caller.  Errors as rs_group_l2norm, and RS_EHIP if the array's device
  * address cannot be obtained. */

@@ -16,12 +16,13 @@
 
 namespace rs {
 
-// Partial sums of the allocation-free L2 norm (rs_group_l2norm_static): one
-// binary64 per workgroup of the first pass, at most kL2Blocks.  Every GPU the
+// Partial sums of the allocation-free L2 norm (rs_group_l2norm_static): two
+// tagged 64-bit words per workgroup, at most kL2Blocks workgroups, then the
+// epoch word (zero at load; each call advances it by one).  Every GPU the
 // library runs on holds its own copy until the process ends, and every call
 // on that GPU shares it.  In host code this name is only a stand-in for the
 // symbol: the device address comes from hipGetSymbolAddress (l2_scratch).
-static __device__ __align__(256) double scratch[kL2Blocks];
+static __device__ __align__(256) double scratch[kL2Words];
 
 namespace {
 
@@ -298,12 +299,33 @@ __device__ __forceinline__ double wg_sum(double v) {
     return s;
 }
 
-// Fixed grid (nwg workgroups); workgroup w takes tiles w, w + nwg, ...
+// Fixed grid (nwg workgroups); workgroup w takes tiles w, w + nwg, ... and
+// publishes its partial sum into slot w; the last workgroup of the grid then
+// collects the nwg partials and adds them in index order, so the result
+// does not depend on timing.  No read-modify-write is involved (2048 atomic
+// additions on one word would serialise at the memory): every call has a
+// sequence number, one more than the epoch word that the previous call left
+// (read by every workgroup at its start: the collector advances it only
+// once every partial of this call is in), and a slot holds the partial's two
+// 32-bit halves, each beside that number in one 64-bit word, so the
+// collector takes a slot only once both words show this call's number.
+// All of it through device-scope atomics, which bypass the per-XCD L2, in
+// relaxed order (a release or acquire at device scope would also write back
+// or invalidate the XCD's whole L2).  The collector's wait is bounded; if it
+// ever gives up (only calls that overlap on one scratch area can make it)
+// the result is NaN.
+constexpr uint32_t kL2SpinLimit = 1u << 22;
+
 template <typename T>
-__global__ __launch_bounds__(kCopyThreads) void sumsq_partial_kernel(Ranges r, const T* __restrict__ buf,
-                                                                     int64_t ntiles, double* part) {
+__global__ __launch_bounds__(kCopyThreads) void sumsq_kernel(Ranges r, const T* __restrict__ buf,
+                                                             int64_t ntiles, uint64_t* slots,
+                                                             double* out) {
     constexpr int V = VecOf<T>::n;
     const int tid = threadIdx.x;
+    uint64_t* epoch = slots + 2 * kL2Blocks;
+    __shared__ uint32_t seq_lds;
+    if (tid == 0)
+        seq_lds = (uint32_t)__hip_atomic_load(epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
     double acc = 0.0;
     for (int64_t wg = blockIdx.x; wg < ntiles; wg += gridDim.x) {
         int64_t t0, t1;
@@ -315,16 +337,44 @@ __global__ __launch_bounds__(kCopyThreads) void sumsq_partial_kernel(Ranges r, c
         for (int64_t p = b0 + int64_t(tid) * V; p < b1; p += int64_t(kCopyThreads) * V)
             acc += sq_vec(load_stream(buf + p), (T*)nullptr);
     }
-    double s = wg_sum(acc);
-    if (tid == 0) part[blockIdx.x] = s;
-}
-
-__global__ __launch_bounds__(kCopyThreads) void sumsq_final_kernel(const double* part, int n,
-                                                                   double* out) {
-    double acc = 0.0;
-    for (int i = threadIdx.x; i < n; i += kCopyThreads) acc += part[i];
-    double s = wg_sum(acc);
-    if (threadIdx.x == 0) *out = s;
+    const double s = wg_sum(acc);  // its barrier also publishes seq_lds
+    const uint64_t seq = (uint64_t)seq_lds << 32;
+    if (tid == 0) {
+        const uint64_t bits = (uint64_t)__double_as_longlong(s);
+        __hip_atomic_store(&slots[2 * blockIdx.x], seq | (bits & 0xffffffffu), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&slots[2 * blockIdx.x + 1], seq | (bits >> 32), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    if (blockIdx.x != gridDim.x - 1) return;
+    __syncthreads();  // thread 0 is done reading wg_sum's LDS before its next use
+    // the collector: every thread takes slots tid, tid + 256, ... (issuing
+    // all of a thread's loads at once measured no faster)
+    const int n = (int)gridDim.x;
+    const uint32_t want = (uint32_t)(seq >> 32);
+    double tot = 0.0;
+    uint32_t spins = 0;
+    bool failed = false;
+    for (int i = tid; i < n; i += kCopyThreads) {
+        uint64_t lo, hi;
+        for (;;) {
+            lo = __hip_atomic_load(&slots[2 * i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            hi = __hip_atomic_load(&slots[2 * i + 1], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((uint32_t)(lo >> 32) == want && (uint32_t)(hi >> 32) == want) break;
+            if (++spins > kL2SpinLimit) {
+                failed = true;
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
+        tot += __longlong_as_double((long long)((hi << 32) | (lo & 0xffffffffu)));
+    }
+    if (failed) tot = __longlong_as_double(0x7ff8000000000000ll);
+    const double t = wg_sum(tot);  // a NaN from any thread reaches the sum
+    if (tid == 0) {
+        *out = t;
+        __hip_atomic_store(epoch, seq >> 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
 }
 
 __global__ void clip_kernel(const double* sumsq, double max_norm, float* scale) {
@@ -390,21 +440,18 @@ hipError_t launch_scale(const Ranges& r, void* buf, int32_t dtype, float f, hipS
     return hipGetLastError();
 }
 
-hipError_t launch_l2norm(const Ranges& r, const void* buf, int32_t dtype, double* d_partials,
+hipError_t launch_l2norm(const Ranges& r, const void* buf, int32_t dtype, double* d_scratch,
                          double* d_out, hipStream_t s) {
     Ranges rr = r;
     int64_t ntiles = tile_ranges(rr);
     int nwg = (int)std::min<int64_t>(std::max<int64_t>(ntiles, 1), kL2Blocks);
+    uint64_t* slots = reinterpret_cast<uint64_t*>(d_scratch);
     if (dtype == RS_BF16)
-        hipLaunchKernelGGL(sumsq_partial_kernel<uint16_t>, dim3(nwg), dim3(kCopyThreads), 0, s,
-                           rr, (const uint16_t*)buf, ntiles, d_partials);
+        hipLaunchKernelGGL(sumsq_kernel<uint16_t>, dim3(nwg), dim3(kCopyThreads), 0, s, rr,
+                           (const uint16_t*)buf, ntiles, slots, d_out);
     else
-        hipLaunchKernelGGL(sumsq_partial_kernel<float>, dim3(nwg), dim3(kCopyThreads), 0, s, rr,
-                           (const float*)buf, ntiles, d_partials);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(sumsq_final_kernel, dim3(1), dim3(kCopyThreads), 0, s, d_partials, nwg,
-                       d_out);
+        hipLaunchKernelGGL(sumsq_kernel<float>, dim3(nwg), dim3(kCopyThreads), 0, s, rr,
+                           (const float*)buf, ntiles, slots, d_out);
     return hipGetLastError();
 }
 

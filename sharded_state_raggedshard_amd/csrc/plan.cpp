@@ -732,7 +732,7 @@ rs_status build_tables(Plan& p, std::string& err) {
     p.off_coop8 = off;
     off = align256(off + p.chunks8.size() * sizeof(PartSlot));
     p.off_l2 = off;
-    off = align256(off + size_t(kL2Blocks) * 8);
+    off = align256(off + size_t(kL2Words) * 8);
     p.off_flag = off;
     off = align256(off + sizeof(CoopCounters));
     p.ws_bytes = off;
