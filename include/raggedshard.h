@@ -169,8 +169,9 @@ rs_status rs_plan_rank_blocks(const rs_plan* plan, int32_t bucket, int32_t rank,
 
 /* Maximum elements one workgroup handles in the step (a multiple of 16 in
  * 64..16384).  Larger blocks are split into chunks.  The planner's default
- * is 8192, or 4096 when most elements sit in tiles narrower than their
- * tensor.  Must be called before rs_plan_upload.  Errors: RS_EINVAL,
+ * is 4096, or 8192 for plans of more than 2^30 elements of which at most
+ * half sit in tiles narrower than their tensor.  Must be called before
+ * rs_plan_upload.  Errors: RS_EINVAL,
  * RS_ESTATE (uploaded). */
 rs_status rs_plan_set_chunk(rs_plan* plan, int64_t chunk_elems);
 

@@ -57,6 +57,12 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
+// 16-byte streaming store (the packed buffer is consumed by the next
+// collective, not by this kernel: non-temporal hint)
+__device__ __forceinline__ void store_stream(void* p, const uint4& v) {
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
 // Which range a workgroup belongs to (ranges are few; uniform scan).
 __device__ __forceinline__ int find_range(const Ranges& r, int64_t wg) {
     int i = 0;
@@ -113,7 +119,7 @@ __device__ __forceinline__ void pack_seg(uint16_t* buf, const float* src, int64_
             o.y = pack2(__uint_as_float(x[2 * u].z), __uint_as_float(x[2 * u].w));
             o.z = pack2(__uint_as_float(x[2 * u + 1].x), __uint_as_float(x[2 * u + 1].y));
             o.w = pack2(__uint_as_float(x[2 * u + 1].z), __uint_as_float(x[2 * u + 1].w));
-            *reinterpret_cast<uint4*>(buf + p0 + u * STEP) = o;
+            store_stream(buf + p0 + u * STEP, o);
         }
     }
     for (int64_t p = p0; p < b1; p += STEP) {
@@ -125,7 +131,7 @@ __device__ __forceinline__ void pack_seg(uint16_t* buf, const float* src, int64_
         o.y = pack2(__uint_as_float(x0.z), __uint_as_float(x0.w));
         o.z = pack2(__uint_as_float(x1.x), __uint_as_float(x1.y));
         o.w = pack2(__uint_as_float(x1.z), __uint_as_float(x1.w));
-        *reinterpret_cast<uint4*>(buf + p) = o;
+        store_stream(buf + p, o);
     }
 }
 
