@@ -57,12 +57,6 @@ __device__ __forceinline__ uint4 load_stream(const void* p) {
     return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-// 16-byte streaming store (the packed buffer is consumed by the next
-// collective, not by this kernel: non-temporal hint)
-__device__ __forceinline__ void store_stream(void* p, const uint4& v) {
-    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
-}
-
 // Which range a workgroup belongs to (ranges are few; uniform scan).
 __device__ __forceinline__ int find_range(const Ranges& r, int64_t wg) {
     int i = 0;
@@ -102,36 +96,25 @@ __device__ __forceinline__ void pack_seg(uint16_t* buf, const float* src, int64_
     int64_t b1 = max(b0, e & ~int64_t(7));
     for (int64_t p = s + tid; p < b0; p += kCopyThreads) buf[p] = f32_to_bf16(src[p - tstart]);
     for (int64_t p = b1 + tid; p < e; p += kCopyThreads) buf[p] = f32_to_bf16(src[p - tstart]);
-    constexpr int64_t STEP = int64_t(kCopyThreads) * 8;
-    int64_t p0 = b0 + int64_t(tid) * 8;
-    for (; p0 + 3 * STEP < b1; p0 += 4 * STEP) {
+    // 2048-element steps; in each, lane t converts elements 4 t .. 4 t + 3 of
+    // the first and of the second 1024, so every load instruction of a wave
+    // reads one contiguous 1 KiB span (and every store writes 512 B)
+    constexpr int64_t STEP = int64_t(kCopyThreads) * 8, HALF = STEP / 2;
+    int64_t p0 = b0 + int64_t(tid) * 4;
+    for (; p0 + 3 * STEP + HALF < b1; p0 += 4 * STEP) {
         uint4 x[8];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const float* sp = src + (p0 + u * STEP - tstart);
-            x[2 * u] = load_stream(sp);
-            x[2 * u + 1] = load_stream(sp + 4);
-        }
+        for (int u = 0; u < 8; ++u) x[u] = load_stream(src + (p0 + u * HALF - tstart));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            uint4 o;
-            o.x = pack2(__uint_as_float(x[2 * u].x), __uint_as_float(x[2 * u].y));
-            o.y = pack2(__uint_as_float(x[2 * u].z), __uint_as_float(x[2 * u].w));
-            o.z = pack2(__uint_as_float(x[2 * u + 1].x), __uint_as_float(x[2 * u + 1].y));
-            o.w = pack2(__uint_as_float(x[2 * u + 1].z), __uint_as_float(x[2 * u + 1].w));
-            store_stream(buf + p0 + u * STEP, o);
-        }
+        for (int u = 0; u < 8; ++u)
+            *reinterpret_cast<uint2*>(buf + p0 + u * HALF) =
+                make_uint2(pack2(__uint_as_float(x[u].x), __uint_as_float(x[u].y)),
+                           pack2(__uint_as_float(x[u].z), __uint_as_float(x[u].w)));
     }
-    for (int64_t p = p0; p < b1; p += STEP) {
-        const float* sp = src + (p - tstart);
-        const uint4 x0 = load_stream(sp);
-        const uint4 x1 = load_stream(sp + 4);
-        uint4 o;
-        o.x = pack2(__uint_as_float(x0.x), __uint_as_float(x0.y));
-        o.y = pack2(__uint_as_float(x0.z), __uint_as_float(x0.w));
-        o.z = pack2(__uint_as_float(x1.x), __uint_as_float(x1.y));
-        o.w = pack2(__uint_as_float(x1.z), __uint_as_float(x1.w));
-        store_stream(buf + p, o);
+    for (int64_t p = p0; p < b1; p += HALF) {
+        const uint4 x = load_stream(src + (p - tstart));
+        *reinterpret_cast<uint2*>(buf + p) = make_uint2(pack2(__uint_as_float(x.x), __uint_as_float(x.y)),
+                                                        pack2(__uint_as_float(x.z), __uint_as_float(x.w)));
     }
 }
 
