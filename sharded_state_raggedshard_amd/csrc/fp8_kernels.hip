@@ -92,13 +92,6 @@ __device__ __forceinline__ uint32_t fp8x4_of(const float4& x, float s, float y) 
                   fp8_ratio(x.w, s, y));
 }
 
-// Tensor (buffer order) holding buffer position pos.
-__device__ __forceinline__ int tensor_at(const TensorTables& tt, int64_t pos) {
-    int j = tt.gidx[pos / kGranule];
-    while (j < tt.n && tt.tend[j] <= pos) ++j;
-    return j;
-}
-
 // n zero bytes from p (p is any byte address of a 16-byte aligned buffer).
 template <int NT>
 __device__ void zero_bytes(uint8_t* p, int64_t n) {
@@ -162,7 +155,7 @@ __device__ __forceinline__ void fp8_pack_chunk(const Fp8Args& a, int64_t c, cons
         zero_bytes<NT>(a.b.buf + d.pos, d.cols);
         return;
     }
-    const int j = tensor_at(a.tt, d.pos);
+    const int j = d.tensor;
     const float* src = reinterpret_cast<const float*>(a.tt.views[j]) + (d.pos - a.tt.tstart[j]);
     if (d.kind == KIND_SCALAR) {
         if (MODE != MODE_PARTIAL)
@@ -276,7 +269,7 @@ __global__ __launch_bounds__(NT) void fp8_pack_kernel(Fp8Args a) {
     }
     if (kCoop && status != 0u && d.kind == KIND_VEC && d.nparts > 1 && d.run_log2 < 0) {
         if (d.part == 0) {
-            const int j = tensor_at(a.tt, d.pos);
+            const int j = d.tensor;
             fp8_block_sweeps<NT>(a.b.chunks + c, d.nparts,
                                  reinterpret_cast<const float*>(a.tt.views[j]), a.tt.tstart[j],
                                  a.b.buf, a.b.scale, red);
@@ -293,7 +286,7 @@ __global__ __launch_bounds__(NT) void fp8_unpack_kernel(Fp8Args a) {
     const int64_t c = chunk_of(a.r, blockIdx.x);
     const ChunkDesc d = a.b.chunks[c];
     if (d.kind == KIND_PAD) return;
-    const int j = tensor_at(a.tt, d.pos);
+    const int j = d.tensor;
     uint16_t* dst = reinterpret_cast<uint16_t*>(a.tt.views[j]) + (d.pos - a.tt.tstart[j]);
     const uint8_t* in = a.b.buf + d.pos;
     const float* scale = a.b.scale;

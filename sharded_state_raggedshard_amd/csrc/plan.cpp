@@ -498,6 +498,7 @@ struct ChunkBuilder {
     const BucketInfo& B;
     int64_t CH;
     std::vector<ChunkDesc>& out;
+    int32_t tj = -1;  // the current tensor's index in buffer order
 
     int32_t rank_of(int64_t pos) const { return (int32_t)((pos - B.base) / B.S); }
 
@@ -512,6 +513,7 @@ struct ChunkBuilder {
         c.nparts = 1;
         c.kind = KIND_SCALAR;
         c.run_log2 = -1;
+        c.tensor = tj;
         out.push_back(c);
     }
 
@@ -526,7 +528,8 @@ struct ChunkBuilder {
         c.part = part;
         c.nparts = nparts;
         c.kind = KIND_VEC;
-        c.run_log2 = run_log2;
+        c.run_log2 = (int16_t)run_log2;
+        c.tensor = tj;
         out.push_back(c);
     }
 
@@ -563,6 +566,7 @@ struct ChunkBuilder {
                 c.nparts = 1;
                 c.kind = KIND_ELEM;
                 c.run_log2 = -1;
+                c.tensor = tj;
                 out.push_back(c);
                 i += len;
             }
@@ -636,6 +640,7 @@ static rs_status build_chunks(const Plan& p, int64_t chunk, bool pad, std::vecto
     const int32_t m = p.m;
     chunks.clear();
     begin.assign(size_t(nb) * (m + 1), 0);
+    int32_t tj = 0;  // buffer-order index of the next tensor
     for (int32_t k = 0; k < nb; ++k) {
         const BucketInfo& B = p.b[k];
         size_t first = chunks.size();
@@ -655,6 +660,7 @@ static rs_status build_chunks(const Plan& p, int64_t chunk, bool pad, std::vecto
                 c.nparts = 1;
                 c.kind = KIND_PAD;
                 c.run_log2 = -1;
+                c.tensor = -1;
                 chunks.push_back(c);
                 cur = e;
             }
@@ -663,6 +669,7 @@ static rs_status build_chunks(const Plan& p, int64_t chunk, bool pad, std::vecto
         for (int32_t i : B.tensors) {
             const TensorInfo& t = p.t[i];
             pad_to(t.pos);
+            cbld.tj = tj++;
             cbld.tensor(t);
             cur = t.pos + t.N;
         }

@@ -30,8 +30,9 @@ struct alignas(16) ChunkDesc {
     int32_t cols;
     int32_t part;
     int32_t nparts;
-    int32_t kind;
-    int32_t run_log2;
+    int16_t kind;
+    int16_t run_log2;
+    int32_t tensor;  // the chunk's tensor in buffer order (-1 for padding)
 };
 static_assert(sizeof(ChunkDesc) == 48, "ChunkDesc layout");
 
