@@ -12,9 +12,12 @@ on its root r, every other rank holding none of it (an uneven RaggedShard:
 per-rank sizes differ) -- Newton-Schulz runs on the root, and the result is
 redistributed back and applied; on the other ranks the matrix update is a
 no-op.  The page's "RaggedShard" section gives the uneven per-device
-distribution this needs.  The Muon update itself is the one of the "Muon
-Optimizer at Scale" entry of the same site (matrix orthogonalisation of 2-D
-updates, decoupled weight decay, a per-matrix scale), read as:
+distribution this needs.  The Muon update itself is the one the "Muon
+Optimizer at Scale" entry of the AI-history comparison page
+(ai-history-trend-future, /history/compare) summarises (matrix
+orthogonalisation of 2-D updates, weight decay and a calibration to the
+parameter scale); the pages give no formulas, so the published form is
+read here as:
 
   M <- mu * M + G                         (binary32, the momentum)
   U  = bf16(M)                            (what the redistribution carries)
