@@ -426,6 +426,8 @@ __global__ __launch_bounds__(GT) void ns_gemm_kernel(GemmArgs g) {
 // ------------------------------------------------ 256 x 256 products
 
 constexpr int T2 = 256, BK2 = 32, NSTAGE = 4;
+constexpr int GT2 = 512;               // eight waves: two per SIMD
+constexpr int kRowsPerWave2 = T2 / (GT2 / 64);
 constexpr int kStage2 = T2 * BK2;      // bf16 of one operand tile in LDS (16 KiB)
 constexpr int kOutR2 = T2 + 8;         // bf16 per row of the staged result tile
 static_assert(T2 * kOutR2 >= 2 * NSTAGE * kStage2, "the staged result tile covers the stages");
@@ -438,7 +440,7 @@ constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) |
 // LDS, straight from global memory (gfx950's 16-byte loads to LDS, no VGPR
 // staging).  LDS rows are 64 bytes; the 16-byte chunk c of row r sits at
 // chunk c ^ ((r >> 2) & 3), so the 16 lanes of a fragment read meet 16
-// different bank groups.  Wave w fills rows [64 w, 64 w + 64), sixteen rows
+// different bank groups.  Wave w fills rows [32 w, 32 w + 32), sixteen rows
 // per instruction (lane l: row l / 4, physical chunk l % 4).  Rows past rmax
 // read row rmax - 1: they only feed results outside the matrix, which are
 // never stored.
@@ -446,13 +448,13 @@ __device__ __forceinline__ void tile_to_lds(const uint16_t* A, int64_t ld, int64
                                             int64_t rmax, int64_t k0, uint16_t* dst) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int row = wave * 64 + j * 16 + (lane >> 2);
+    for (int j = 0; j < kRowsPerWave2 / 16; ++j) {
+        const int row = wave * kRowsPerWave2 + j * 16 + (lane >> 2);
         const int lc = (lane & 3) ^ ((row >> 2) & 3);
         int64_t gr = r0 + row;
         gr = gr < rmax ? gr : rmax - 1;
         __builtin_amdgcn_global_load_lds(A + gr * ld + k0 + lc * 8,
-                                         dst + (wave * 64 + j * 16) * BK2, 16, 0, 0);
+                                         dst + (wave * kRowsPerWave2 + j * 16) * BK2, 16, 0, 0);
     }
 }
 
@@ -460,15 +462,16 @@ __device__ __forceinline__ bf16x8 frag2(const uint16_t* src, int row, int lc) {
     return *reinterpret_cast<const bf16x8*>(src + row * BK2 + ((lc ^ ((row >> 2) & 3)) << 3));
 }
 
-// One 256 x 256 tile of a product whose K is a multiple of 32.  Four waves,
-// each a 128 x 128 quarter as 4 x 4 MFMA tiles (256 accumulators per lane);
-// both operand tiles go straight to LDS through four stages, loads issued
-// three stages ahead of the multiplications so that their latency is hidden
-// behind three stages of MFMA work.  The addend is read through its
+// One 256 x 256 tile of a product whose K is a multiple of 32.  Eight waves
+// (two per SIMD, so one wave's LDS reads and barrier overlap the other's
+// MFMAs), each a 128 x 64 part as 4 x 2 MFMA tiles (128 accumulators per
+// lane); both operand tiles go straight to LDS through four stages, loads
+// issued three stages ahead of the multiplications so that their latency is
+// hidden behind three stages of MFMA work.  The addend is read through its
 // transpose Rt (A itself, or X for Y), so the four consecutive rows a lane
 // holds for one column are 8 contiguous bytes.  One workgroup per compute
 // unit (132 KiB of LDS).
-__global__ __launch_bounds__(GT) void ns_gemm256_kernel(GemmArgs g) {
+__global__ __launch_bounds__(GT2) void ns_gemm256_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[T2 * kOutR2];
     const int nm = g.t.nm;
     const int64_t* pre = g.t.tiles + (int64_t)g.table * (nm + 1);
@@ -479,19 +482,20 @@ __global__ __launch_bounds__(GT) void ns_gemm256_kernel(GemmArgs g) {
     tile_of_product(g, p, tg - pre[mi], T2, tm, tn);
     const int64_t m0 = tm * T2, n0 = tn * T2;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+    constexpr int TI = 4, TJ = 2;  // MFMA tiles of a wave: 128 rows x 64 columns
+    const int wm = wave >> 2, wn = wave & 3;
 
     const int frow = lane & 31, half = lane >> 5;
     // lane l holds column l % 32 of each 32 x 32 MFMA tile, register r its
     // row 8 (r / 4) + 4 (l / 32) + r % 4: four consecutive rows per register
     // group
     auto row_of = [&](int i, int q) { return wm * 128 + i * 32 + 8 * q + 4 * half; };
-    auto col_of = [&](int j) { return wn * 128 + j * 32 + frow; };
-    f32x16 acc[4][4];
+    auto col_of = [&](int j) { return wn * 64 + j * 32 + frow; };
+    f32x16 acc[TI][TJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
     const int KT = (int)(p.K / BK2);
@@ -503,14 +507,15 @@ __global__ __launch_bounds__(GT) void ns_gemm256_kernel(GemmArgs g) {
     for (int s = 0; s < NSTAGE - 1; ++s)
         if (s < KT) issue(s);
     for (int kt = 0; kt < KT; ++kt) {
-        // stage kt has landed once at most the later stages' loads (8 per
+        // stage kt has landed once at most the later stages' loads (4 per
         // stage per wave) are outstanding; the barrier then also tells every
         // wave that all are done reading the stage the next issue overwrites
+        constexpr int kPerStage = 2 * (kRowsPerWave2 / 16);
         const int later = min(NSTAGE - 2, KT - 1 - kt);
         if (later >= 2)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(16));
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerStage));
         else if (later == 1)
-            __builtin_amdgcn_s_waitcnt(vmcnt_imm(8));
+            __builtin_amdgcn_s_waitcnt(vmcnt_imm(kPerStage));
         else
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
         // a bare barrier (also a compiler memory fence): __syncthreads would
@@ -520,27 +525,27 @@ __global__ __launch_bounds__(GT) void ns_gemm256_kernel(GemmArgs g) {
         if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
         const uint16_t* sp = lds + (kt % NSTAGE) * 2 * kStage2;
         const uint16_t* sq = sp + kStage2;
-        // every fragment of the stage is read up front (16 reads), then the 32
+        // every fragment of the stage is read up front (12 reads), then the 16
         // MFMAs run back to back
-        bf16x8 fa[BK2 / 16][4], fb[BK2 / 16][4];
+        bf16x8 fa[BK2 / 16][TI], fb[BK2 / 16][TJ];
 #pragma unroll
         for (int kk = 0; kk < BK2 / 16; ++kk) {
             const int lc = 2 * kk + half;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) fa[kk][i] = frag2(sp, wm * 128 + i * 32 + frow, lc);
+            for (int i = 0; i < TI; ++i) fa[kk][i] = frag2(sp, wm * 128 + i * 32 + frow, lc);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) fb[kk][j] = frag2(sq, wn * 128 + j * 32 + frow, lc);
+            for (int j = 0; j < TJ; ++j) fb[kk][j] = frag2(sq, wn * 64 + j * 32 + frow, lc);
         }
 #pragma unroll
         for (int kk = 0; kk < BK2 / 16; ++kk)
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < TI; ++i)
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
+                for (int j = 0; j < TJ; ++j)
                     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j],
                                                                         acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 16, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 32, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, (BK2 / 16) * (TI + TJ), 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, (BK2 / 16) * TI * TJ, 0);
     }
     __syncthreads();  // every wave is done with the stages: LDS is free
     // results alpha acc + beta R, straight then transposed, each staged
@@ -566,9 +571,9 @@ __global__ __launch_bounds__(GT) void ns_gemm256_kernel(GemmArgs g) {
         uint2 rcur[4], rnxt[4];
         load_r(0, 0, rcur);
 #pragma unroll
-        for (int ij = 0; ij < 16; ++ij) {
-            const int i = ij >> 2, j = ij & 3;
-            if (ij + 1 < 16) load_r((ij + 1) >> 2, (ij + 1) & 3, rnxt);
+        for (int ij = 0; ij < TI * TJ; ++ij) {
+            const int i = ij / TJ, j = ij % TJ;
+            if (ij + 1 < TI * TJ) load_r((ij + 1) / TJ, (ij + 1) % TJ, rnxt);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -595,7 +600,7 @@ __global__ __launch_bounds__(GT) void ns_gemm256_kernel(GemmArgs g) {
         const int64_t ra = pass == 0 ? m0 : n0, ca = pass == 0 ? n0 : m0;
         const int64_t rlim = pass == 0 ? p.M : p.N, clim = pass == 0 ? p.N : p.M;
         const int64_t ld = pass == 0 ? p.ldc : p.ldct;
-        for (int v = tid; v < T2 * (T2 / 8); v += GT) {
+        for (int v = tid; v < T2 * (T2 / 8); v += GT2) {
             const int rr = v / (T2 / 8), c8 = (v % (T2 / 8)) * 8;
             if (ra + rr < rlim && ca + c8 < clim)
                 *reinterpret_cast<uint4*>(out + (ra + rr) * ld + ca + c8) =
@@ -669,7 +674,7 @@ hipError_t launch_orthogonalize(const Tables& t, const int64_t* host_tiles, int3
             a.root = root;
             if (wide) {
                 a.table = 4 + kind;
-                hipLaunchKernelGGL(ns_gemm256_kernel, dim3((unsigned)count(4 + kind)), dim3(GT), 0,
+                hipLaunchKernelGGL(ns_gemm256_kernel, dim3((unsigned)count(4 + kind)), dim3(GT2), 0,
                                    s, a);
             } else {
                 a.table = 1 + kind;
