@@ -548,65 +548,66 @@ __global__ __launch_bounds__(GT2) void ns_gemm256_kernel(GemmArgs g) {
         __builtin_amdgcn_sched_group_barrier(0x008, (BK2 / 16) * TI * TJ, 0);
     }
     __syncthreads();  // every wave is done with the stages: LDS is free
-    // results alpha acc + beta R, straight then transposed, each staged
-    // through LDS and stored as 16-byte row pieces (M, N and the leading
-    // dimensions are multiples of 8)
+    // results bf16(alpha acc + beta R), stored straight and/or transposed as
+    // 16-byte row pieces through an LDS tile (M, N and the leading dimensions
+    // are multiples of 8).  The addend's tile (rows m0 .., columns n0 .. of
+    // the row-major R) first comes into that LDS tile with coalesced 16-byte
+    // row loads; each lane then replaces its own elements by the results,
+    // keeping them packed for the transposed store.
     uint16_t* so = lds;
-    // addend of 32 x 32 tile (i, j), register group q: 8 bytes of Rt
-    auto load_r = [&](int i, int j, uint2 (&w)[4]) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int row = row_of(i, q), col = col_of(j);
-            w[q] = make_uint2(0u, 0u);
-            if (p.Rt && m0 + row < p.M && n0 + col < p.N)
-                w[q] = *reinterpret_cast<const uint2*>(p.Rt + (n0 + col) * p.ldrt + m0 + row);
-        }
+    auto tile_rows = [&](auto&& body) {
+        for (int v = tid; v < T2 * (T2 / 8); v += GT2) body(v / (T2 / 8), (v % (T2 / 8)) * 8);
     };
-    for (int pass = 0; pass < 2; ++pass) {
-        uint16_t* out = pass == 0 ? p.Cs : p.Ct;
-        if (!out) continue;
-        // the addend of the next 32 x 32 tile is in flight while this one is
-        // formed (one tile's loads at a time: the scheduler barrier keeps the
-        // compiler from hoisting all 64 of them)
-        uint2 rcur[4], rnxt[4];
-        load_r(0, 0, rcur);
+    if (p.Rr) {
+        tile_rows([&](int rr, int c8) {
+            uint4 w = make_uint4(0u, 0u, 0u, 0u);
+            if (m0 + rr < p.M && n0 + c8 < p.N)
+                w = *reinterpret_cast<const uint4*>(p.Rr + (m0 + rr) * p.ldr + n0 + c8);
+            *reinterpret_cast<uint4*>(so + rr * kOutR2 + c8) = w;
+        });
+        __syncthreads();
+    }
+    uint32_t hp[TI][TJ][4][2];  // results, bf16 pairs of rows (r, r + 1)
 #pragma unroll
-        for (int ij = 0; ij < TI * TJ; ++ij) {
-            const int i = ij / TJ, j = ij % TJ;
-            if (ij + 1 < TI * TJ) load_r((ij + 1) / TJ, (ij + 1) % TJ, rnxt);
-            __builtin_amdgcn_sched_barrier(0);
+    for (int i = 0; i < TI; ++i)
+#pragma unroll
+        for (int j = 0; j < TJ; ++j)
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 const int row = row_of(i, q), col = col_of(j);
-                const float rv[4] = {bf16_val(rcur[q].x & 0xffffu), bf16_val(rcur[q].x >> 16),
-                                     bf16_val(rcur[q].y & 0xffffu), bf16_val(rcur[q].y >> 16)};
                 uint32_t h[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    h[r] = bf16_bits(p.alpha * acc[i][j][4 * q + r] + p.beta * rv[r]);
-                if (pass == 0) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) so[(row + r) * kOutR2 + col] = (uint16_t)h[r];
-                } else {
-                    *reinterpret_cast<uint2*>(so + col * kOutR2 + row) =
-                        make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+                for (int r = 0; r < 4; ++r) {
+                    uint16_t* e = so + (row + r) * kOutR2 + col;
+                    const float rv = p.Rr ? bf16_val(*e) : 0.0f;
+                    h[r] = bf16_bits(p.alpha * acc[i][j][4 * q + r] + p.beta * rv);
+                    *e = (uint16_t)h[r];
                 }
+                hp[i][j][q][0] = h[0] | (h[1] << 16);
+                hp[i][j][q][1] = h[2] | (h[3] << 16);
             }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) rcur[q] = rnxt[q];
-        }
-        __syncthreads();
-        const int64_t ra = pass == 0 ? m0 : n0, ca = pass == 0 ? n0 : m0;
-        const int64_t rlim = pass == 0 ? p.M : p.N, clim = pass == 0 ? p.N : p.M;
-        const int64_t ld = pass == 0 ? p.ldc : p.ldct;
-        for (int v = tid; v < T2 * (T2 / 8); v += GT2) {
-            const int rr = v / (T2 / 8), c8 = (v % (T2 / 8)) * 8;
+    __syncthreads();
+    auto store_tile = [&](uint16_t* out, int64_t ra, int64_t ca, int64_t rlim, int64_t clim,
+                          int64_t ld) {
+        tile_rows([&](int rr, int c8) {
             if (ra + rr < rlim && ca + c8 < clim)
                 *reinterpret_cast<uint4*>(out + (ra + rr) * ld + ca + c8) =
                     *reinterpret_cast<const uint4*>(so + rr * kOutR2 + c8);
-        }
+        });
+    };
+    if (p.Cs) store_tile(p.Cs, m0, n0, p.M, p.N, p.ldc);
+    if (p.Ct) {
+        if (p.Cs) __syncthreads();  // the straight tile is out of LDS
+#pragma unroll
+        for (int i = 0; i < TI; ++i)
+#pragma unroll
+            for (int j = 0; j < TJ; ++j)
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<uint2*>(so + col_of(j) * kOutR2 + row_of(i, q)) =
+                        make_uint2(hp[i][j][q][0], hp[i][j][q][1]);
         __syncthreads();
+        store_tile(p.Ct, n0, m0, p.N, p.M, p.ldct);
     }
 }
 
