@@ -4,15 +4,18 @@ Headline workload: the whole Llama-8B-shaped state on one rank (8.03e9
 fp32 master parameters, 291 tensors, 32-row quantisation blocks, m = 1),
 the largest configuration that fits one GPU.  One step = one pass of the
 whole hot path over one batch of synthetic gradients, in stream order:
-    group_l2norm(grad) -> clip_coef -> adam8_step(grad scale = the clip
-    coefficient, fused bf16 copy-in into the gathered buffer) ->
+    group_l2norm_clip(grad: the global sum of squares and the clipping
+    coefficient in one launch; with m = 1 the whole norm is on this device) ->
+    adam8_step(grad scale = the clip coefficient, fused bf16 copy-in into
+    the gathered buffer) ->
     unpack_full(gathered buffer -> per-parameter bf16 views) ->
     group_zero(the gradient buffer the next backward pass accumulates into)
 Two seeded random gradient buffers alternate between steps, so every step
 reads a full gradient.  Inputs are resident in HBM before the timed region;
 a step streams about 200 GB, far beyond the 256 MB last-level cache, so
-nothing is served from cache.  After the K timed steps, the step without
-the fused output, the standalone copy-in (pack_shard) and the FP8 copy-in /
+nothing is served from cache.  After the K timed steps, the L2 norm alone
+(the form an m-GPU job uses, before its all-reduce), the step without the
+fused output, the standalone copy-in (pack_shard) and the FP8 copy-in /
 copy-out are timed on their own (K calls each, HIP events).
 
 `per_config` then times every op of the other workloads on their own
@@ -95,6 +98,7 @@ def algorithmic_bytes(real, buf, blocks, unpack_real, unpack_blocks):
         "unpack_full": 4 * unpack_real,
         # read / write bf16 over the whole selection
         "group_l2norm": 2 * buf,
+        "group_l2norm_clip": 2 * buf,
         "group_zero": 2 * buf,
         # read fp32 4 + write code 1 per element; zero padding 1; write scale 4 per block
         "pack_shard_fp8": 5 * real + pad + 4 * blocks,
@@ -222,6 +226,9 @@ class Bench:
             rs.rs_group_l2norm(p, rs.RS_ALL, R, grad, rs.RS_BF16, self.sumsq, stream=sid)
         elif name == "clip_coef":
             rs.rs_clip_coef(self.sumsq, 1.0, self.scale, stream=sid)
+        elif name == "group_l2norm_clip":
+            rs.rs_group_l2norm_clip(p, rs.RS_ALL, R, grad, rs.RS_BF16, 1.0, self.sumsq, self.scale,
+                                    stream=sid)
         elif name == "adam8_step":
             rs.rs_adam8_step(p, rs.RS_ALL, R, self.theta, grad, self.qm, self.qv, self.am, self.av,
                              step=t, grad_scale=self.scale, stream=sid)
@@ -274,8 +281,8 @@ class Bench:
         torch.cuda.empty_cache()
 
 
-STEP_OPS = ["group_l2norm", "clip_coef", "adam8_step_bf16_out", "unpack_full", "group_zero"]
-ALONE_OPS = ["adam8_step", "pack_shard", "pack_shard_fp8", "unpack_full_fp8"]
+STEP_OPS = ["group_l2norm_clip", "adam8_step_bf16_out", "unpack_full", "group_zero"]
+ALONE_OPS = ["group_l2norm", "adam8_step", "pack_shard", "pack_shard_fp8", "unpack_full_fp8"]
 CONFIG_OPS = ["group_l2norm", "adam8_step", "pack_shard", "unpack_full", "group_zero",
               "pack_shard_fp8", "unpack_full_fp8"]
 

@@ -290,8 +290,19 @@ rs_status rs_group_l2norm_static(const rs_plan* plan, int32_t bucket, int32_t ra
                                  const void* d_buf, int32_t dtype, double* d_sumsq, void* stream);
 
 /* Gradient-clipping coefficient on the device:
- * *d_scale = (float) min(1, max_norm / (sqrt(*d_sumsq) + 1e-6)), in binary64. */
+ * *d_scale = (float) min(1, max_norm / (sqrt(*d_sumsq) + 1e-6)), in binary64.
+ * Separate from the norm because on m GPUs the per-rank sums of squares are
+ * all-reduced between the two. */
 rs_status rs_clip_coef(const double* d_sumsq, double max_norm, float* d_scale, void* stream);
+
+/* rs_group_l2norm and rs_clip_coef in one launch, for a selection that is
+ * the whole norm (every rank of the buckets on this device, or m = 1):
+ * *d_sumsq as rs_group_l2norm, *d_scale as rs_clip_coef for max_norm, bit
+ * for bit.  d_scale: one device float, 4-byte aligned.  Errors as
+ * rs_group_l2norm, and RS_EINVAL for max_norm not finite and > 0. */
+rs_status rs_group_l2norm_clip(const rs_plan* plan, int32_t bucket, int32_t rank, const void* d_buf,
+                               int32_t dtype, double max_norm, double* d_sumsq, float* d_scale,
+                               void* stream);
 
 /* ----------------------------------------------------------- int8 AdamW */
 

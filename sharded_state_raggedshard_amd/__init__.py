@@ -36,7 +36,7 @@ EXPORTS = (
     "rs_plan_device_bytes", "rs_plan_upload", "rs_bind_views", "rs_pack_shard", "rs_unpack_full",
     "rs_pack_shard_fp8", "rs_unpack_full_fp8",
     "rs_group_zero", "rs_group_scale", "rs_group_l2norm", "rs_group_l2norm_static",
-    "rs_clip_coef", "rs_adam8_step",
+    "rs_clip_coef", "rs_group_l2norm_clip", "rs_adam8_step",
     "rs_plan_check_device", "rs_plan_status_offset", "rs_last_error", "rs_version",
     "rs_muon_plan", "rs_muon_free", "rs_muon_layout", "rs_muon_device_bytes", "rs_muon_upload",
     "rs_muon_gather", "rs_muon_orthogonalize", "rs_muon_apply",
@@ -100,6 +100,7 @@ def lib() -> C.CDLL:
         "rs_group_l2norm": ([vp, i32, i32, vp, i32, vp, vp], C.c_int),
         "rs_group_l2norm_static": ([vp, i32, i32, vp, i32, vp, vp], C.c_int),
         "rs_clip_coef": ([vp, C.c_double, vp, vp], C.c_int),
+        "rs_group_l2norm_clip": ([vp, i32, i32, vp, i32, C.c_double, vp, vp, vp], C.c_int),
         "rs_adam8_step": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, C.POINTER(rs_adam_hparams), vp,
                            vp, vp], C.c_int),
         "rs_plan_check_device": ([vp, vp], C.c_int),
@@ -284,6 +285,12 @@ def rs_group_l2norm_static(plan: int, bucket: int, rank: int, buf, dtype: int, s
 
 def rs_clip_coef(sumsq, max_norm: float, scale, stream=None) -> None:
     _check(lib().rs_clip_coef(_ptr(sumsq), max_norm, _ptr(scale), _stream(stream)))
+
+
+def rs_group_l2norm_clip(plan: int, bucket: int, rank: int, buf, dtype: int, max_norm: float,
+                         sumsq, scale, stream=None) -> None:
+    _check(lib().rs_group_l2norm_clip(plan, bucket, rank, _ptr(buf), dtype, max_norm, _ptr(sumsq),
+                                      _ptr(scale), _stream(stream)))
 
 
 def rs_adam8_step(plan: int, bucket: int, rank: int, master, grad, qm, qv, amax_m, amax_v,

@@ -444,7 +444,7 @@ rs_status rs_group_l2norm(const rs_plan* plan, int32_t bucket, int32_t rank, con
     std::vector<rs::Ranges> g = groups(elem_ranges(p, bucket, rank));
     if (g.size() != 1) return fail(RS_EINVAL, "selection has more slices than one launch takes");
     hipError_t e = rs::launch_l2norm(g[0], d_buf, dtype, reinterpret_cast<double*>(ws(p, p.off_l2)),
-                                     d_sumsq, as_stream(stream));
+                                     d_sumsq, 0.0, nullptr, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, "l2norm launch");
     return RS_OK;
 }
@@ -469,7 +469,28 @@ rs_status rs_group_l2norm_static(const rs_plan* plan, int32_t bucket, int32_t ra
         return fail(RS_EINVAL, "the norm needs " + std::to_string(need) +
                                    " partial sums; the library's array holds " +
                                    std::to_string(capacity));
-    e = rs::launch_l2norm(g[0], d_buf, dtype, partials, d_sumsq, as_stream(stream));
+    e = rs::launch_l2norm(g[0], d_buf, dtype, partials, d_sumsq, 0.0, nullptr, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "l2norm launch");
+    return RS_OK;
+}
+
+rs_status rs_group_l2norm_clip(const rs_plan* plan, int32_t bucket, int32_t rank, const void* d_buf,
+                               int32_t dtype, double max_norm, double* d_sumsq, float* d_scale,
+                               void* stream) {
+    if (!plan || !d_buf || !d_sumsq || !d_scale) return fail(RS_EINVAL, "NULL argument");
+    if (!aligned(d_buf, 16) || !aligned(d_sumsq, 8) || !aligned(d_scale, 4))
+        return fail(RS_EINVAL, "misaligned pointer");
+    if (!(max_norm > 0.0) || !std::isfinite(max_norm)) return fail(RS_EINVAL, "max_norm must be finite and > 0");
+    rs_status st = check_dtype(dtype);
+    if (st != RS_OK) return st;
+    const rs::Plan& p = plan->p;
+    st = check_sel(p, bucket, rank);
+    if (st != RS_OK) return st;
+    if (!p.uploaded) return fail(RS_ESTATE, "plan not uploaded (the norm uses workspace scratch)");
+    std::vector<rs::Ranges> g = groups(elem_ranges(p, bucket, rank));
+    if (g.size() != 1) return fail(RS_EINVAL, "selection has more slices than one launch takes");
+    hipError_t e = rs::launch_l2norm(g[0], d_buf, dtype, reinterpret_cast<double*>(ws(p, p.off_l2)),
+                                     d_sumsq, max_norm, d_scale, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, "l2norm launch");
     return RS_OK;
 }

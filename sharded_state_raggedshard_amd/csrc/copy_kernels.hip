@@ -288,6 +288,14 @@ __device__ __forceinline__ double wg_sum(double v) {
     return s;
 }
 
+// Clipping coefficient min(1, max_norm / (sqrt(sumsq) + 1e-6)), binary64,
+// rounded once to binary32.
+__device__ __forceinline__ float clip_of(double sumsq, double max_norm) {
+    double c = max_norm / (sqrt(sumsq) + 1e-6);
+    if (c > 1.0) c = 1.0;
+    return (float)c;
+}
+
 // Fixed grid (nwg workgroups); workgroup w takes tiles w, w + nwg, ... and
 // publishes its partial sum into slot w; the last workgroup of the grid then
 // collects the nwg partials and adds them in index order, so the result
@@ -308,7 +316,8 @@ constexpr uint32_t kL2SpinLimit = 1u << 22;
 template <typename T>
 __global__ __launch_bounds__(kCopyThreads) void sumsq_kernel(Ranges r, const T* __restrict__ buf,
                                                              int64_t ntiles, uint64_t* slots,
-                                                             double* out) {
+                                                             double* out, double max_norm,
+                                                             float* scale) {
     constexpr int V = VecOf<T>::n;
     const int tid = threadIdx.x;
     uint64_t* epoch = slots + 2 * kL2Blocks;
@@ -362,16 +371,13 @@ __global__ __launch_bounds__(kCopyThreads) void sumsq_kernel(Ranges r, const T* 
     const double t = wg_sum(tot);  // a NaN from any thread reaches the sum
     if (tid == 0) {
         *out = t;
+        if (scale) *scale = clip_of(t, max_norm);
         __hip_atomic_store(epoch, seq >> 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
 }
 
 __global__ void clip_kernel(const double* sumsq, double max_norm, float* scale) {
-    if (threadIdx.x == 0 && blockIdx.x == 0) {
-        double c = max_norm / (sqrt(*sumsq) + 1e-6);
-        if (c > 1.0) c = 1.0;
-        *scale = (float)c;
-    }
+    if (threadIdx.x == 0 && blockIdx.x == 0) *scale = clip_of(*sumsq, max_norm);
 }
 
 }  // namespace
@@ -430,17 +436,17 @@ hipError_t launch_scale(const Ranges& r, void* buf, int32_t dtype, float f, hipS
 }
 
 hipError_t launch_l2norm(const Ranges& r, const void* buf, int32_t dtype, double* d_scratch,
-                         double* d_out, hipStream_t s) {
+                         double* d_out, double max_norm, float* d_scale, hipStream_t s) {
     Ranges rr = r;
     int64_t ntiles = tile_ranges(rr);
     int nwg = (int)std::min<int64_t>(std::max<int64_t>(ntiles, 1), kL2Blocks);
     uint64_t* slots = reinterpret_cast<uint64_t*>(d_scratch);
     if (dtype == RS_BF16)
         hipLaunchKernelGGL(sumsq_kernel<uint16_t>, dim3(nwg), dim3(kCopyThreads), 0, s, rr,
-                           (const uint16_t*)buf, ntiles, slots, d_out);
+                           (const uint16_t*)buf, ntiles, slots, d_out, max_norm, d_scale);
     else
         hipLaunchKernelGGL(sumsq_kernel<float>, dim3(nwg), dim3(kCopyThreads), 0, s, rr,
-                           (const float*)buf, ntiles, slots, d_out);
+                           (const float*)buf, ntiles, slots, d_out, max_norm, d_scale);
     return hipGetLastError();
 }
 

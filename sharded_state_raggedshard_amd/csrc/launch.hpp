@@ -44,9 +44,11 @@ hipError_t launch_unpack(const Ranges& r, const TensorTables& tt, const uint16_t
 hipError_t launch_zero(const Ranges& r, void* buf, int32_t dtype, hipStream_t s);
 hipError_t launch_scale(const Ranges& r, void* buf, int32_t dtype, float f, hipStream_t s);
 // One launch; d_scratch: kL2Words 64-bit words (tagged partial sums, then
-// an epoch word that each call advances; zero when first used).
+// an epoch word that each call advances; zero when first used).  With
+// d_scale, the same launch also writes the clipping coefficient for
+// max_norm.
 hipError_t launch_l2norm(const Ranges& r, const void* buf, int32_t dtype, double* d_scratch,
-                         double* d_out, hipStream_t s);
+                         double* d_out, double max_norm, float* d_scale, hipStream_t s);
 hipError_t launch_clip(const double* d_sumsq, double max_norm, float* d_scale, hipStream_t s);
 
 // Partial sums the L2 norm of ranges r writes (one per first-pass workgroup).

@@ -220,6 +220,8 @@ def test_invalid_specs_and_arguments():
     _expect(rs.RS_ESTATE, rs.rs_pack_shard, h, 0, 0, fake, stream=0)
     _expect(rs.RS_ESTATE, rs.rs_unpack_full, h, 0, fake, stream=0)
     _expect(rs.RS_ESTATE, rs.rs_group_l2norm, h, 0, 0, fake, rs.RS_BF16, fake, stream=0)
+    _expect(rs.RS_ESTATE, rs.rs_group_l2norm_clip, h, 0, 0, fake, rs.RS_BF16, 1.0, fake, fake,
+            stream=0)
     _expect(rs.RS_ESTATE, rs.rs_adam8_step, h, 0, 0, fake, fake, fake, fake, fake, fake, stream=0)
     _expect(rs.RS_ESTATE, rs.rs_bind_views, h, rs.RS_VIEW_F32_SRC, [fake], stream=0)
     _expect(rs.RS_ESTATE, rs.rs_plan_check_device, h, stream=0)
@@ -232,10 +234,28 @@ def test_invalid_specs_and_arguments():
     _expect(rs.RS_EINVAL, rs.rs_adam8_step, h, 0, 0, fake, fake + 8, fake, fake, fake, fake,
             stream=0)
     _expect(rs.RS_EINVAL, rs.rs_clip_coef, fake, -1.0, fake, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_group_l2norm_clip, h, 0, 0, fake, rs.RS_BF16, 0.0, fake, fake,
+            stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_group_l2norm_clip, h, 0, 0, fake, rs.RS_BF16, 1.0, fake, fake + 2,
+            stream=0)
     _expect(rs.RS_EINVAL, rs.rs_plan_upload, h, fake + 16, 1 << 30, stream=0)
     _expect(rs.RS_ENOMEM, rs.rs_plan_upload, h, fake, 16, stream=0)
     assert "workspace" in rs.rs_last_error()
     rs.rs_plan_free(h)
+
+
+def test_threaded_scan_is_deterministic():
+    # the DeepSeek-V3-shaped MoE layer at 128-row blocks and m = 16 finishes
+    # its scan on several threads: the plan is the same on every call
+    specs = [TensorSpec(s.name, s.shape, s.gran, s.br, s.bc, 0)
+             for s in synth.MODEL_SHAPES["deepseek_v3"](128) if s.bucket == 4]
+    first = None
+    for _ in range(5):
+        h = rs.rs_plan_layout(specs, 16, 16)
+        got = (rs.rs_plan_bucket(h, 0), rs.rs_plan_offsets(h))
+        rs.rs_plan_free(h)
+        first = first or got
+        assert got == first
 
 
 def test_replanning_is_deterministic():

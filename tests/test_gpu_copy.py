@@ -165,6 +165,14 @@ def test_l2norm_and_clip_coefficient():
         assert math.isclose(math.sqrt(got), math.sqrt(exp), rel_tol=1e-5)
         # the coefficient from the device sum equals the oracle's formula on it
         assert scale.item() == oracle.clip_coef(got, 1.0)
+        # the fused norm-and-clip launch gives both bit for bit, for a
+        # threshold that clips (sigma = 1) and one that does not
+        for max_norm in (1.0, 1e6):
+            s2 = torch.full((1,), -1.0, dtype=torch.float64, device="cuda")
+            c2 = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
+            rs.rs_group_l2norm_clip(plan.h, rs.RS_ALL, rs.RS_ALL, dev, rs.RS_BF16, max_norm, s2, c2)
+            assert s2.cpu().numpy().view(np.uint64)[0] == sumsq.cpu().numpy().view(np.uint64)[0]
+            assert c2.item() == oracle.clip_coef(got, max_norm)
         # per-rank partial sums add up to the global sum
         parts = 0.0
         for r in range(m):
