@@ -146,6 +146,10 @@ def test_group_ops(name, dtype):
     plan.free()
 
 
+def _clip_formula(sumsq: float, max_norm: float) -> float:
+    return float(np.float32(min(1.0, max_norm / (math.sqrt(sumsq) + 1e-6))))
+
+
 def test_l2norm_and_clip_coefficient():
     specs, m, g = LAYOUTS["llama_layer"]()
     L = oracle.Layout(specs, m, g)
@@ -163,8 +167,11 @@ def test_l2norm_and_clip_coefficient():
         got = float(sumsq.item())
         exp = L.group_sumsq(-1, -1, host)
         assert math.isclose(math.sqrt(got), math.sqrt(exp), rel_tol=1e-5)
-        # the coefficient from the device sum equals the oracle's formula on it
-        assert scale.item() == oracle.clip_coef(got, 1.0)
+        # the coefficient: the oracle's, from the oracle's sum, to the sum's
+        # tolerance; and exactly the formula (binary64, one rounding) applied
+        # to the device's own sum
+        assert math.isclose(scale.item(), oracle.clip_coef(exp, 1.0), rel_tol=1e-5)
+        assert scale.item() == _clip_formula(got, 1.0)
         # the fused norm-and-clip launch gives both bit for bit, for a
         # threshold that clips (sigma = 1) and one that does not
         for max_norm in (1.0, 1e6):
@@ -172,7 +179,8 @@ def test_l2norm_and_clip_coefficient():
             c2 = torch.full((1,), -1.0, dtype=torch.float32, device="cuda")
             rs.rs_group_l2norm_clip(plan.h, rs.RS_ALL, rs.RS_ALL, dev, rs.RS_BF16, max_norm, s2, c2)
             assert s2.cpu().numpy().view(np.uint64)[0] == sumsq.cpu().numpy().view(np.uint64)[0]
-            assert c2.item() == oracle.clip_coef(got, max_norm)
+            assert c2.item() == _clip_formula(got, max_norm)
+            assert math.isclose(c2.item(), oracle.clip_coef(exp, max_norm), rel_tol=1e-5)
         # per-rank partial sums add up to the global sum
         parts = 0.0
         for r in range(m):

@@ -64,7 +64,7 @@ def _check_pack(L, plan, hv, dv, bucket, rank):
         detail = [(int(i), float(x[i]), int(got[i]), int(exp[i])) for i in bad[:6]]
         raise AssertionError(f"{bad.size} codes differ; (pos, x, got, expected): {detail}")
     assert np.array_equal(sc.cpu().numpy().view(np.uint32), esc.view(np.uint32))
-    return buf, sc
+    return buf, sc, exp, esc
 
 
 @pytest.mark.parametrize("mode", [rs.RS_SPLIT_TWO_PASS, rs.RS_SPLIT_COOPERATIVE,
@@ -79,7 +79,7 @@ def test_fp8_pack_unpack_bitexact(name, mode):
     hv = _views(specs, 7)
     dv = [torch.from_numpy(v).cuda() for v in hv]
     rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, dv)
-    buf, sc = _check_pack(L, plan, hv, dv, rs.RS_ALL, rs.RS_ALL)
+    buf, sc, hbuf, hsc = _check_pack(L, plan, hv, dv, rs.RS_ALL, rs.RS_ALL)
     # per-slice calls touch only their slice and reproduce the whole
     for r in sorted({0, m // 2, m - 1}):
         _check_pack(L, plan, hv, dv, rs.RS_ALL, r)
@@ -88,7 +88,7 @@ def test_fp8_pack_unpack_bitexact(name, mode):
     rs.rs_bind_views(plan.h, rs.RS_VIEW_BF16_DST, outs)
     rs.rs_unpack_full_fp8(plan.h, rs.RS_ALL, buf, sc)
     hexp = [np.zeros(s.numel, dtype=np.uint16) for s in specs]
-    L.unpack_fp8(-1, hexp, buf.cpu().numpy(), sc.cpu().numpy())
+    L.unpack_fp8(-1, hexp, hbuf, hsc)  # the oracle's own pack, equal to the device's
     for s, o, e in zip(specs, outs, hexp):
         assert np.array_equal(dev_to_u16(o), e), s.name
     if mode != rs.RS_SPLIT_TWO_PASS:
@@ -138,12 +138,12 @@ def test_fp8_every_code_and_tie():
           small.reshape(-1).astype(np.float32)]
     dv = [torch.from_numpy(v).cuda() for v in hv]
     rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, dv)
-    buf, sc = _check_pack(L, plan, hv, dv, rs.RS_ALL, rs.RS_ALL)
+    buf, sc, hbuf, hsc = _check_pack(L, plan, hv, dv, rs.RS_ALL, rs.RS_ALL)
     outs = [torch.zeros(s.numel, dtype=torch.int16, device="cuda") for s in specs]
     rs.rs_bind_views(plan.h, rs.RS_VIEW_BF16_DST, outs)
     rs.rs_unpack_full_fp8(plan.h, rs.RS_ALL, buf, sc)
     hexp = [np.zeros(s.numel, dtype=np.uint16) for s in specs]
-    L.unpack_fp8(-1, hexp, buf.cpu().numpy(), sc.cpu().numpy())
+    L.unpack_fp8(-1, hexp, hbuf, hsc)  # the oracle's own pack, equal to the device's
     for s, o, e in zip(specs, outs, hexp):
         assert np.array_equal(dev_to_u16(o), e), s.name
     plan.free()

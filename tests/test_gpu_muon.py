@@ -138,7 +138,7 @@ def test_orthogonalize_against_oracle(name):
     got = dev_to_u16(root)
     for k, (R, C) in enumerate(shapes):
         u = oracle.bf16_to_f32(U[mu.offsets[k]:mu.offsets[k] + R * C]).reshape(R, C)
-        o = oracle.bf16_to_f32(got[mu.offsets[k]:mu.offsets[k] + R * C]).reshape(R, C)
+        o = (got[mu.offsets[k]:mu.offsets[k] + R * C].astype(np.uint32) << 16).view(np.float32).reshape(R, C)
         _check_O(o.astype(np.float64), u.astype(np.float64), f"{specs[mats[k]].name} {R}x{C}")
     mu.free()
     plan.free()

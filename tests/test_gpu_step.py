@@ -87,11 +87,18 @@ def _run_free(name, mode, chunk, steps=3, per_rank=False, warm=False, gscale=Non
         assert (got.theta[pad] == 7.0).all()
         out = dev_to_u16(ds.out)
         assert (out[pad] == 0).all()
-        assert np.array_equal(out[~pad], oracle.bf16(got.theta[~pad]))
+        assert np.array_equal(out[~pad], _torch_bf16(got.theta[~pad]))
     if mode != TWO:
         rs.rs_plan_check_device(plan.h)
     plan.free()
     return got
+
+
+def _torch_bf16(x: np.ndarray) -> np.ndarray:
+    """bf16 bits of float32 values by torch's round-to-nearest-even
+    conversion: the fused output must be the bf16 of the returned master
+    (a property of the kernel's own outputs; the oracle is not used on them)."""
+    return torch.from_numpy(np.ascontiguousarray(x)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
 
 
 @pytest.mark.parametrize("mode", [TWO, COOP, ORD])
@@ -250,7 +257,7 @@ def test_status_word_set_takes_wait_free_path_exactly(name, chunk, mode):
         assert np.array_equal(got.am, ref.am) and np.array_equal(got.av, ref.av)
         assert (got.qm[pad] == SENT_CODE).all() and (got.theta[pad] == 7.0).all()
         out = dev_to_u16(ds.out)
-        assert np.array_equal(out[~pad], oracle.bf16(got.theta[~pad]))
+        assert np.array_equal(out[~pad], _torch_bf16(got.theta[~pad]))
         if t < 13:
             with pytest.raises(rs.RaggedShardError) as ei:
                 rs.rs_plan_check_device(plan.h)
