@@ -102,6 +102,8 @@ def algorithmic_bytes(real, buf, blocks, unpack_real, unpack_blocks):
         "group_zero": 2 * buf,
         # read fp32 4 + write code 1 per element; zero padding 1; write scale 4 per block
         "pack_shard_fp8": 5 * real + pad + 4 * blocks,
+        # the step with FP8 output: the step + code write 1 per element, scale 4 per block
+        "adam8_step_fp8": 15 * real + 20 * blocks,
         # read code 1 + write bf16 2 per element; read scale 4 per block
         "unpack_full_fp8": 3 * unpack_real + 4 * unpack_blocks,
     }
@@ -235,6 +237,10 @@ class Bench:
         elif name == "adam8_step_bf16_out":
             rs.rs_adam8_step(p, rs.RS_ALL, R, self.theta, grad, self.qm, self.qv, self.am, self.av,
                              step=t, grad_scale=self.scale, bf16_out=self.gathered, stream=sid)
+        elif name == "adam8_step_fp8":
+            rs.rs_adam8_step_fp8(p, rs.RS_ALL, R, self.theta, grad, self.qm, self.qv, self.am,
+                                 self.av, self.codes8, self.scale8, step=t,
+                                 grad_scale=self.scale, stream=sid)
         elif name == "pack_shard":
             rs.rs_pack_shard(p, rs.RS_ALL, R, self.gathered, stream=sid)
         elif name == "unpack_full":
@@ -282,9 +288,10 @@ class Bench:
 
 
 STEP_OPS = ["group_l2norm_clip", "adam8_step_bf16_out", "unpack_full", "group_zero"]
-ALONE_OPS = ["group_l2norm", "adam8_step", "pack_shard", "pack_shard_fp8", "unpack_full_fp8"]
+ALONE_OPS = ["group_l2norm", "adam8_step", "pack_shard", "pack_shard_fp8", "unpack_full_fp8",
+             "adam8_step_fp8"]
 CONFIG_OPS = ["group_l2norm", "adam8_step", "pack_shard", "unpack_full", "group_zero",
-              "pack_shard_fp8", "unpack_full_fp8"]
+              "pack_shard_fp8", "unpack_full_fp8", "adam8_step_fp8"]
 
 
 def time_steps(bn, steps, warmup):

@@ -328,6 +328,29 @@ rs_status rs_adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float
                         float* d_amax_v, const rs_adam_hparams* hp, const float* d_grad_scale,
                         uint16_t* d_bf16_out, void* stream);
 
+/* rs_adam8_step followed by the FP8 copy-in of the new parameters, in one
+ * pass (page sections "Structure-aware training case study", 8-bit Adam, and
+ * "Problem and motivation", block-wise FP8: both work on the same
+ * quantisation blocks, which RaggedShard keeps inside one rank).  Every
+ * output of rs_adam8_step as there (d_bf16_out nullable), and for every
+ * block B of the selection the FP8 rule of rs_pack_shard_fp8 applied to the
+ * new parameters theta' (the values written to d_master):
+ *   d_fp8_scale[B] = max|theta'| / 448 (binary32),
+ *   d_fp8[i] = E4M3 code of theta'[i] / d_fp8_scale[B] (correctly rounded
+ *              quotient, ties to even, saturating; scale 0 gives code 0),
+ * so the codes and scales are exactly those rs_pack_shard_fp8 gives for
+ * views holding theta'.  d_fp8: one byte per buffer element (full
+ * bucket-set array, 16-byte aligned); padding positions are not written
+ * (rs_pack_shard_fp8 writes them 0; they stay so).  d_fp8_scale: one float
+ * per global block id.  Saves the copy-in's separate read of the master
+ * (4 bytes per element) and its own cross-chunk wait on split blocks.
+ * Errors: as rs_adam8_step; RS_EINVAL if d_fp8 or d_fp8_scale is NULL. */
+rs_status rs_adam8_step_fp8(const rs_plan* plan, int32_t bucket, int32_t rank, float* d_master,
+                            const uint16_t* d_grad, int8_t* d_qm, uint8_t* d_qv,
+                            float* d_amax_m, float* d_amax_v, const rs_adam_hparams* hp,
+                            const float* d_grad_scale, uint16_t* d_bf16_out, uint8_t* d_fp8,
+                            float* d_fp8_scale, void* stream);
+
 /* ------------------------------------------------------- distributed Muon
  * veScale-FSDP page, section "Structure-aware training case study",
  * distributed Muon (Algorithm 2), with the uneven per-device distribution of

@@ -36,7 +36,7 @@ EXPORTS = (
     "rs_plan_device_bytes", "rs_plan_upload", "rs_bind_views", "rs_pack_shard", "rs_unpack_full",
     "rs_pack_shard_fp8", "rs_unpack_full_fp8",
     "rs_group_zero", "rs_group_scale", "rs_group_l2norm", "rs_group_l2norm_static",
-    "rs_clip_coef", "rs_group_l2norm_clip", "rs_adam8_step",
+    "rs_clip_coef", "rs_group_l2norm_clip", "rs_adam8_step", "rs_adam8_step_fp8",
     "rs_plan_check_device", "rs_plan_status_offset", "rs_last_error", "rs_version",
     "rs_muon_plan", "rs_muon_free", "rs_muon_layout", "rs_muon_device_bytes", "rs_muon_upload",
     "rs_muon_gather", "rs_muon_orthogonalize", "rs_muon_apply",
@@ -103,6 +103,8 @@ def lib() -> C.CDLL:
         "rs_group_l2norm_clip": ([vp, i32, i32, vp, i32, C.c_double, vp, vp, vp], C.c_int),
         "rs_adam8_step": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, C.POINTER(rs_adam_hparams), vp,
                            vp, vp], C.c_int),
+        "rs_adam8_step_fp8": ([vp, i32, i32, vp, vp, vp, vp, vp, vp, C.POINTER(rs_adam_hparams),
+                               vp, vp, vp, vp, vp], C.c_int),
         "rs_plan_check_device": ([vp, vp], C.c_int),
         "rs_plan_status_offset": ([vp, C.POINTER(C.c_size_t)], C.c_int),
         "rs_muon_plan": ([vp, P32, i32, C.POINTER(vp)], C.c_int),
@@ -300,6 +302,19 @@ def rs_adam8_step(plan: int, bucket: int, rank: int, master, grad, qm, qv, amax_
     _check(lib().rs_adam8_step(plan, bucket, rank, _ptr(master), _ptr(grad), _ptr(qm), _ptr(qv),
                                _ptr(amax_m), _ptr(amax_v), C.byref(hp), _ptr(grad_scale),
                                _ptr(bf16_out), _stream(stream)))
+
+
+def rs_adam8_step_fp8(plan: int, bucket: int, rank: int, master, grad, qm, qv, amax_m, amax_v,
+                      fp8, fp8_scale, lr=1e-3, beta1=0.9, beta2=0.999, eps=1e-8,
+                      weight_decay=0.01, step=1, grad_scale=None, bf16_out=None,
+                      stream=None) -> None:
+    """rs_adam8_step plus the FP8 codes (uint8, one per buffer element) and
+    block scales (fp32 per global block) of the new master."""
+    hp = rs_adam_hparams(lr, beta1, beta2, eps, weight_decay, int(step))
+    _check(lib().rs_adam8_step_fp8(plan, bucket, rank, _ptr(master), _ptr(grad), _ptr(qm),
+                                   _ptr(qv), _ptr(amax_m), _ptr(amax_v), C.byref(hp),
+                                   _ptr(grad_scale), _ptr(bf16_out), _ptr(fp8),
+                                   _ptr(fp8_scale), _stream(stream)))
 
 
 def rs_plan_check_device(plan: int, stream=None) -> None:

@@ -503,15 +503,22 @@ rs_status rs_clip_coef(const double* d_sumsq, double max_norm, float* d_scale, v
     return RS_OK;
 }
 
-rs_status rs_adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float* d_master,
-                        const uint16_t* d_grad, int8_t* d_qm, uint8_t* d_qv, float* d_amax_m,
-                        float* d_amax_v, const rs_adam_hparams* hp, const float* d_grad_scale,
-                        uint16_t* d_bf16_out, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The step with its optional outputs: bf16 (d_bf16_out) and FP8 (d_fp8 and
+// d_fp8_scale, both or neither).
+rs_status adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float* d_master,
+                     const uint16_t* d_grad, int8_t* d_qm, uint8_t* d_qv, float* d_amax_m,
+                     float* d_amax_v, const rs_adam_hparams* hp, const float* d_grad_scale,
+                     uint16_t* d_bf16_out, uint8_t* d_fp8, float* d_fp8_scale, void* stream) {
     if (!plan || !d_master || !d_grad || !d_qm || !d_qv || !d_amax_m || !d_amax_v || !hp)
         return fail(RS_EINVAL, "NULL argument");
     if (!aligned(d_master, 16) || !aligned(d_grad, 16) || !aligned(d_qm, 16) || !aligned(d_qv, 16) ||
         !aligned(d_amax_m, 4) || !aligned(d_amax_v, 4) || (d_grad_scale && !aligned(d_grad_scale, 4)) ||
-        (d_bf16_out && !aligned(d_bf16_out, 16)))
+        (d_bf16_out && !aligned(d_bf16_out, 16)) || (d_fp8 && !aligned(d_fp8, 16)) ||
+        (d_fp8_scale && !aligned(d_fp8_scale, 4)))
         return fail(RS_EINVAL, "misaligned pointer");
     const rs::Plan& p = plan->p;
     rs_status st = check_sel(p, bucket, rank);
@@ -545,12 +552,38 @@ rs_status rs_adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float
     b.cpart = reinterpret_cast<rs::ChunkPartial*>(ws(p, p.off_cpart));
     b.coop = reinterpret_cast<rs::PartSlot*>(ws(p, p.off_coop));
     b.counters = reinterpret_cast<rs::CoopCounters*>(ws(p, p.off_flag));
+    b.fp8 = d_fp8;
+    b.fp8_scale = d_fp8_scale;
+    b.cpart_t = reinterpret_cast<float*>(ws(p, p.off_cpart_t));
+    b.coop_t = reinterpret_cast<rs::PartSlot*>(ws(p, p.off_coop_t));
     for (const rs::Ranges& r : groups(chunk_ranges(p, bucket, rank))) {
         hipError_t e = rs::launch_adam8(r, b, sc, p.split_mode, p.chunk_elems, p.max_nparts,
                                         as_stream(stream));
         if (e != hipSuccess) return hip_fail(e, "adam8 launch");
     }
     return RS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+rs_status rs_adam8_step(const rs_plan* plan, int32_t bucket, int32_t rank, float* d_master,
+                        const uint16_t* d_grad, int8_t* d_qm, uint8_t* d_qv, float* d_amax_m,
+                        float* d_amax_v, const rs_adam_hparams* hp, const float* d_grad_scale,
+                        uint16_t* d_bf16_out, void* stream) {
+    return adam8_step(plan, bucket, rank, d_master, d_grad, d_qm, d_qv, d_amax_m, d_amax_v, hp,
+                      d_grad_scale, d_bf16_out, nullptr, nullptr, stream);
+}
+
+rs_status rs_adam8_step_fp8(const rs_plan* plan, int32_t bucket, int32_t rank, float* d_master,
+                            const uint16_t* d_grad, int8_t* d_qm, uint8_t* d_qv,
+                            float* d_amax_m, float* d_amax_v, const rs_adam_hparams* hp,
+                            const float* d_grad_scale, uint16_t* d_bf16_out, uint8_t* d_fp8,
+                            float* d_fp8_scale, void* stream) {
+    if (!d_fp8 || !d_fp8_scale) return fail(RS_EINVAL, "NULL argument");
+    return adam8_step(plan, bucket, rank, d_master, d_grad, d_qm, d_qv, d_amax_m, d_amax_v, hp,
+                      d_grad_scale, d_bf16_out, d_fp8, d_fp8_scale, stream);
 }
 
 rs_status rs_plan_check_device(rs_plan* plan, void* stream) {

@@ -35,6 +35,13 @@
 // wave then polls the slots of its block (see adam8_kernel for why the waits
 // end).  Each wait is bounded all the same and reports a timeout through the
 // device status word if it ever gives up.
+//
+// FP8 output (the step followed by the FP8 copy-in of the new parameters,
+// in one pass): the new parameters are formed before the block maxima are
+// exchanged, their block absmax travels with those of m and v, and after
+// the wait the lane encodes its parameters, still in registers, as E4M3
+// codes of the block scale absmax / 448.  The copy-in's extra read of the
+// parameters and its own wait disappear; one byte per element is added.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -140,7 +147,7 @@ struct VecIn {
 
 // Issues every load of a vector chunk.  Tile chunks keep rows * ld < 2^30,
 // so a uniform chunk base plus 32-bit lane offsets addresses every element.
-template <int MODE, int KG>
+template <int MODE, int KG, bool F8>
 __device__ __forceinline__ void vec_load(const ChunkDesc& d, int64_t c, const StepBuffers& B,
                                          VecIn<KG>& in) {
     constexpr int WSPAN = 256 * KG;
@@ -185,7 +192,7 @@ __device__ __forceinline__ void vec_load(const ChunkDesc& d, int64_t c, const St
             gw = ld_u2(g_b + p[k]);
             cm = ld_u1(qm_b + p[k]);
             cv = ld_u1(qv_b + p[k]);
-            if (MODE != MODE_PARTIAL) th = ld_f4(th_b + p[k]);
+            if (MODE != MODE_PARTIAL || F8) th = ld_f4(th_b + p[k]);
         }
         in.GW[k] = gw;
         in.CM[k] = cm;
@@ -198,15 +205,34 @@ __device__ __forceinline__ void vec_load(const ChunkDesc& d, int64_t c, const St
 template <int KG>
 struct VecState {
     float M[4 * KG], V[4 * KG];  // new moments of this lane's elements
+    float T[4 * KG];             // new parameters (FP8 output only)
     float am[KG], av[KG];        // new absmax of the block(s) of each slice
+    float at[KG];                // new parameters' absmax (FP8 output only)
     uint32_t seq;                // sequence number published (cooperative split)
     bool wait;                   // the block's other chunks must be waited for
 };
 
+// New parameters of this lane's slice k: the hardware square root and
+// reciprocal, or correctly rounded operations where param_fast asks for them.
+template <int KG>
+__device__ __forceinline__ void new_params(const StepScalars& sc, const float4& th,
+                                           const float* M, const float* V, float (&t)[4]) {
+    const float t0[4] = {th.x, th.y, th.z, th.w};
+    bool exact = false;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) t[j] = param_fast(sc, t0[j], M[j], V[j], exact);
+    if (__builtin_expect(exact, 0)) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) t[j] = param(sc, t0[j], M[j], sqrtf(V[j]));
+    }
+}
+
 // Front: moments and the new block maxima; a cooperative split chunk
-// publishes its maxima.  Returns false when nothing is left to do (the
+// publishes its maxima.  With FP8 output (F8) the new parameters and their
+// block maximum are formed here too, so they travel with the moments'
+// maxima in the same wait.  Returns false when nothing is left to do (the
 // partial pass of a split chunk).
-template <int MODE, int NT, int KG>
+template <int MODE, int NT, int KG, bool F8>
 __device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const StepArgs& a,
                                           float s, const float* dqm, const float* dqv,
                                           float* red, const VecIn<KG>& in, VecState<KG>& st) {
@@ -217,14 +243,14 @@ __device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const S
     // 0 reads it before the workgroup max's barriers and every thread takes
     // it from LDS after them, so no thread can read the slot after thread 0
     // has published into it.
-    uint32_t* seq_lds = reinterpret_cast<uint32_t*>(red + 2 * (NT / 64));
+    uint32_t* seq_lds = reinterpret_cast<uint32_t*>(red + (F8 ? 3 : 2) * (NT / 64));
     if (MODE == MODE_COOP && split && d.run_log2 < 0 && threadIdx.x == 0)
         *seq_lds = coop_seq(B.coop, c);
     st.seq = 0u;
     st.wait = false;
-    float lm[KG], lv[KG];
+    float lm[KG], lv[KG], lt[KG];
 #pragma unroll
-    for (int k = 0; k < KG; ++k) lm[k] = lv[k] = 0.0f;
+    for (int k = 0; k < KG; ++k) lm[k] = lv[k] = lt[k] = 0.0f;
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
         const float g[4] = {bf16_lo(in.GW[k].x) * s, bf16_hi(in.GW[k].x) * s,
@@ -238,6 +264,21 @@ __device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const S
             lv[k] = fmaxf(lv[k], st.V[4 * k + j]);
         }
     }
+    if (F8) {
+        uint32_t p[KG];
+        bool act[KG];
+        lane_offsets<KG>(d, p, act);
+#pragma unroll
+        for (int k = 0; k < KG; ++k) {
+            float t[4];
+            new_params<KG>(sc, in.TH[k], st.M + 4 * k, st.V + 4 * k, t);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                st.T[4 * k + j] = t[j];
+                if (act[k]) lt[k] = fmaxf(lt[k], fabsf(t[j]));
+            }
+        }
+    }
     if (d.run_log2 >= 0) {
         // blocks of (1 << run_log2) elements = (1 << run_log2) / 4 lanes of one slice
         const int lanes = (1 << d.run_log2) >> 2;
@@ -245,14 +286,16 @@ __device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const S
         for (int k = 0; k < KG; ++k) {
             st.am[k] = lm[k];
             st.av[k] = lv[k];
+            st.at[k] = lt[k];
             for (int off = 1; off < lanes; off <<= 1) {
                 st.am[k] = fmaxf(st.am[k], __shfl_xor(st.am[k], off, 64));
                 st.av[k] = fmaxf(st.av[k], __shfl_xor(st.av[k], off, 64));
+                if (F8) st.at[k] = fmaxf(st.at[k], __shfl_xor(st.at[k], off, 64));
             }
         }
         return true;
     }
-    float x, y;
+    float x, y, t = 0.0f;
     if (MODE == MODE_MAIN && split) {
         x = 0.0f;
         y = 0.0f;
@@ -261,36 +304,55 @@ __device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const S
             const ChunkPartial cp = B.cpart[c0 + q];
             x = fmaxf(x, cp.pm);
             y = fmaxf(y, cp.pv);
+            if (F8) t = fmaxf(t, B.cpart_t[c0 + q]);
         }
     } else {
         x = lm[0];
         y = lv[0];
+        t = lt[0];
 #pragma unroll
         for (int k = 1; k < KG; ++k) {
             x = fmaxf(x, lm[k]);
             y = fmaxf(y, lv[k]);
+            if (F8) t = fmaxf(t, lt[k]);
         }
-        wg_max2<NT>(x, y, red);
+        if (F8) {
+            float v[3] = {x, y, t};
+            wg_maxn<NT, 3>(v, red);
+            x = v[0];
+            y = v[1];
+            t = v[2];
+        } else {
+            wg_max2<NT>(x, y, red);
+        }
         if (split) {
             if (MODE == MODE_PARTIAL) {
-                if (threadIdx.x == 0) B.cpart[c] = ChunkPartial{x, y, in.amo[0], in.avo[0]};
+                if (threadIdx.x == 0) {
+                    B.cpart[c] = ChunkPartial{x, y, in.amo[0], in.avo[0]};
+                    if (F8) B.cpart_t[c] = t;
+                }
                 return false;
             }
-            st.seq = *seq_lds;  // written before wg_max2's barriers
+            st.seq = *seq_lds;  // written before the workgroup max's barriers
             st.wait = true;
-            if (threadIdx.x == 0) coop_publish(B.coop, c, st.seq, x, y);
+            if (threadIdx.x == 0) {
+                coop_publish(B.coop, c, st.seq, x, y);
+                if (F8) coop_store(&B.coop_t[c].m, st.seq, t);
+            }
         }
     }
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
         st.am[k] = x;
         st.av[k] = y;
+        st.at[k] = t;
     }
     return true;
 }
 
-// Parameters: needs no absmax, so it runs before any wait.
-template <int KG>
+// Parameters: needs no absmax, so it runs before any wait (with FP8 output
+// they were formed in the front).
+template <int KG, bool F8>
 __device__ __forceinline__ void vec_params(const ChunkDesc& d, const StepArgs& a,
                                            const VecIn<KG>& in, const VecState<KG>& st) {
     const StepScalars& sc = a.sc;
@@ -302,16 +364,12 @@ __device__ __forceinline__ void vec_params(const ChunkDesc& d, const StepArgs& a
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
         if (!act[k]) continue;
-        const float t0[4] = {in.TH[k].x, in.TH[k].y, in.TH[k].z, in.TH[k].w};
         float t[4];
-        bool exact = false;
+        if (F8) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            t[j] = param_fast(sc, t0[j], st.M[4 * k + j], st.V[4 * k + j], exact);
-        if (__builtin_expect(exact, 0)) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                t[j] = param(sc, t0[j], st.M[4 * k + j], sqrtf(st.V[4 * k + j]));
+            for (int j = 0; j < 4; ++j) t[j] = st.T[4 * k + j];
+        } else {
+            new_params<KG>(sc, in.TH[k], st.M + 4 * k, st.V + 4 * k, t);
         }
         st_f4(th_b + p[k], t[0], t[1], t[2], t[3]);
         if (out_b)
@@ -321,8 +379,9 @@ __device__ __forceinline__ void vec_params(const ChunkDesc& d, const StepArgs& a
 }
 
 // Back: waits for the block's other chunks if needed (wave 0 polls, the
-// others wait at a barrier), then quantises and stores codes and absmax.
-template <int NT, int KG>
+// others wait at a barrier), then quantises and stores codes and absmax
+// (and, with FP8 output, the parameters' E4M3 codes and block scale).
+template <int NT, int KG, bool F8>
 __device__ __forceinline__ void vec_back(const ChunkDesc& d, int64_t c, const StepArgs& a,
                                          VecState<KG>& st, float* red) {
     constexpr int WSPAN = 256 * KG;
@@ -335,15 +394,23 @@ __device__ __forceinline__ void vec_back(const ChunkDesc& d, int64_t c, const St
     int8_t* qm_b = B.qm + d.pos;
     uint8_t* qv_b = B.qv + d.pos;
     if (st.wait) {
-        float x, y;
-        // red[0..1] are free again after the workgroup max
-        coop_wait_wg<NT>(B.coop, B.counters, c - d.part, d.nparts, st.seq, red, x, y);
+        float x, y, t = 0.0f;
+        // red[0..2] are free again after the workgroup max
+        coop_wait_wg_t<NT, F8>(B.coop, B.coop_t, B.counters, c - d.part, d.nparts, st.seq, red,
+                               x, y, t);
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             st.am[k] = x;
             st.av[k] = y;
+            st.at[k] = t;
         }
     }
+    uint8_t* f8_b = F8 ? B.fp8 + d.pos : nullptr;
+    auto enc = [&](int k, float s8, float y8) {
+        st_u1(f8_b + p[k], fp8x4_of(make_float4(st.T[4 * k], st.T[4 * k + 1], st.T[4 * k + 2],
+                                                st.T[4 * k + 3]),
+                                    s8, y8));
+    };
     // |m| <= absmax bounds the codes: no clamp; int8 via a +128 offset
     auto quant = [&](int k, float a_m, float a_v, float ym, float yv) {
         uint32_t qmw = 0u, qvw = 0u;
@@ -374,10 +441,13 @@ __device__ __forceinline__ void vec_back(const ChunkDesc& d, int64_t c, const St
         for (int k = 0; k < KG; ++k) {
             if (!act[k]) continue;
             quant(k, st.am[k], st.av[k], quant_recip(st.am[k]), quant_recip(st.av[k]));
+            const float s8 = F8 ? st.at[k] / 448.0f : 0.0f;
+            if (F8) enc(k, s8, quant_recip(s8));
             if ((lane & (lanes - 1)) == 0) {
                 const int64_t blk = d.blk + ((wave * WSPAN + 256 * k + 4 * lane) >> d.run_log2);
                 B.amax_m[blk] = st.am[k];
                 B.amax_v[blk] = st.av[k];
+                if (F8) B.fp8_scale[blk] = s8;
             }
         }
     } else {
@@ -387,34 +457,44 @@ __device__ __forceinline__ void vec_back(const ChunkDesc& d, int64_t c, const St
 #pragma unroll
         for (int k = 0; k < KG; ++k)
             if (act[k]) quant(k, a_m, a_v, ym, yv);
+        const float s8 = F8 ? st.at[0] / 448.0f : 0.0f;
+        if (F8) {
+            const float y8 = quant_recip(s8);
+#pragma unroll
+            for (int k = 0; k < KG; ++k)
+                if (act[k]) enc(k, s8, y8);
+        }
         if (threadIdx.x == 0 && d.part == 0) {
             B.amax_m[d.blk] = a_m;
             B.amax_v[d.blk] = a_v;
+            if (F8) B.fp8_scale[d.blk] = s8;
         }
     }
 }
 
 // The whole update of one vector chunk from its loaded inputs.
-template <int MODE, int NT, int KG>
+template <int MODE, int NT, int KG, bool F8>
 __device__ __forceinline__ void vec_process(const ChunkDesc& d, int64_t c, const StepArgs& a,
                                             float s, const float* dqm, const float* dqv,
                                             float* red, const VecIn<KG>& in) {
     VecState<KG> st;
-    if (!vec_front<MODE, NT, KG>(d, c, a, s, dqm, dqv, red, in, st)) return;
-    if (MODE != MODE_PARTIAL) vec_params<KG>(d, a, in, st);
-    vec_back<NT, KG>(d, c, a, st, red);
+    if (!vec_front<MODE, NT, KG, F8>(d, c, a, s, dqm, dqv, red, in, st)) return;
+    if (MODE != MODE_PARTIAL) vec_params<KG, F8>(d, a, in, st);
+    vec_back<NT, KG, F8>(d, c, a, st, red);
 }
 
 // --------------------------------------------------- generic block paths
 
 // One whole block, two sweeps (absmax, then update and codes), element by
 // element over its pieces ds[0 .. nd): any shape, stride or alignment.
-template <int NT>
+// With FP8 output the first sweep forms the new parameters too, for their
+// absmax (the second forms them again, the same values).
+template <int NT, bool F8>
 __device__ void block_sweeps(const ChunkDesc* ds, int nd, int64_t blk, const StepArgs& a,
                              float s, const float* dqm, const float* dqv, float* red) {
     const StepBuffers& B = a.b;
     const float am_old = B.amax_m[blk], av_old = B.amax_v[blk];
-    float lam = 0.0f, lav = 0.0f;
+    float lam = 0.0f, lav = 0.0f, lat = 0.0f;
     for (int q = 0; q < nd; ++q) {
         const ChunkDesc d = ds[q];
         const int64_t n = int64_t(d.rows) * d.cols;
@@ -424,13 +504,23 @@ __device__ void block_sweeps(const ChunkDesc* ds, int nd, int64_t blk, const Ste
             const float g = __uint_as_float(uint32_t(B.grad[p]) << 16) * s;
             const float mh = dqm[uint8_t(B.qm[p])] * am_old;
             const float vh = dqv[B.qv[p]] * av_old;
-            const Elem el = update(a.sc, 0.0f, g, mh, vh);
+            const Elem el = update(a.sc, F8 ? B.theta[p] : 0.0f, g, mh, vh);
             lam = fmaxf(lam, fabsf(el.m));
             lav = fmaxf(lav, el.v);
+            if (F8) lat = fmaxf(lat, fabsf(el.th));
         }
     }
-    wg_max2<NT>(lam, lav, red);
+    if (F8) {
+        float v[3] = {lam, lav, lat};
+        wg_maxn<NT, 3>(v, red);
+        lam = v[0];
+        lav = v[1];
+        lat = v[2];
+    } else {
+        wg_max2<NT>(lam, lav, red);
+    }
     const float ym = quant_recip(lam), yv = quant_recip(lav);
+    const float s8 = lat / 448.0f, y8 = quant_recip(s8);
     for (int q = 0; q < nd; ++q) {
         const ChunkDesc d = ds[q];
         const int64_t n = int64_t(d.rows) * d.cols;
@@ -443,6 +533,7 @@ __device__ void block_sweeps(const ChunkDesc* ds, int nd, int64_t blk, const Ste
             const Elem el = update(a.sc, B.theta[p], g, mh, vh);
             B.theta[p] = el.th;
             if (B.out) B.out[p] = (uint16_t)f32_to_bf16(el.th);
+            if (F8) B.fp8[p] = (uint8_t)fp8_of(el.th, s8, y8);
             B.qm[p] = (int8_t)code_m(el.m, lam, ym);
             B.qv[p] = (uint8_t)code_v(el.v, lav, yv);
         }
@@ -450,12 +541,13 @@ __device__ void block_sweeps(const ChunkDesc* ds, int nd, int64_t blk, const Ste
     if (threadIdx.x == 0) {
         B.amax_m[blk] = lam;
         B.amax_v[blk] = lav;
+        if (F8) B.fp8_scale[blk] = s8;
     }
 }
 
 // A run of single-element blocks: the absmax is the element itself, so the
 // codes are +-127 / 255 (or 0) and the state is lossless.
-template <int NT>
+template <int NT, bool F8>
 __device__ void elem_chunk(const ChunkDesc& d, const StepArgs& a, float s, const float* dqm,
                            const float* dqv) {
     const StepBuffers& B = a.b;
@@ -468,6 +560,11 @@ __device__ void elem_chunk(const ChunkDesc& d, const StepArgs& a, float s, const
         const Elem el = update(a.sc, B.theta[p], g, mh, vh);
         B.theta[p] = el.th;
         if (B.out) B.out[p] = (uint16_t)f32_to_bf16(el.th);
+        if (F8) {
+            const float s8 = fabsf(el.th) / 448.0f;
+            B.fp8[p] = (uint8_t)fp8_of(el.th, s8, quant_recip(s8));
+            B.fp8_scale[blk] = s8;
+        }
         const float am = fabsf(el.m), av = el.v;
         B.qm[p] = (int8_t)code_m(el.m, am, quant_recip(am));
         B.qv[p] = (uint8_t)code_v(el.v, av, quant_recip(av));
@@ -487,20 +584,20 @@ __device__ __forceinline__ void fill_tables(float* dqm, float* dqv) {
 }
 
 // One chunk, start to end.
-template <int MODE, int NT, int KG>
+template <int MODE, int NT, int KG, bool F8>
 __device__ __forceinline__ void one_chunk(const ChunkDesc& d, int64_t c, const StepArgs& a, float s,
                                           const float* dqm, const float* dqv, float* red) {
     // the partial pass only visits chunks of split blocks
     if (MODE == MODE_PARTIAL && (d.kind != KIND_VEC || d.nparts == 1)) return;
     if (d.kind == KIND_VEC) {
         VecIn<KG> in;
-        vec_load<MODE, KG>(d, c, a.b, in);
-        vec_process<MODE, NT, KG>(d, c, a, s, dqm, dqv, red, in);
+        vec_load<MODE, KG, F8>(d, c, a.b, in);
+        vec_process<MODE, NT, KG, F8>(d, c, a, s, dqm, dqv, red, in);
     } else if (MODE != MODE_PARTIAL) {
         if (d.kind == KIND_SCALAR)
-            block_sweeps<NT>(a.b.chunks + c, 1, d.blk, a, s, dqm, dqv, red);
+            block_sweeps<NT, F8>(a.b.chunks + c, 1, d.blk, a, s, dqm, dqv, red);
         else
-            elem_chunk<NT>(d, a, s, dqm, dqv);
+            elem_chunk<NT, F8>(d, a, s, dqm, dqv);
     }
 }
 
@@ -526,11 +623,15 @@ __device__ __forceinline__ void one_chunk(const ChunkDesc& d, int64_t c, const S
 // whole block in two sweeps and the block's other chunks do nothing.  A
 // timeout thus costs time, not state, until rs_plan_check_device clears
 // the word.
-template <int MODE, int NT, int KG>
+//
+// F8: the step with FP8 output (the new parameters' E4M3 codes and block
+// scales, the FP8 copy-in's rule); a separate instance of every mode.
+template <int MODE, int NT, int KG, bool F8>
 __global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
     constexpr bool kCoop = MODE == MODE_COOP || MODE == MODE_ORDERED;
     __shared__ float dqm[256], dqv[256];
-    __shared__ float red[2 * (NT / 64) + 2];
+    // the workgroup max (2 or 3 values per wave), then the sequence word
+    __shared__ float red[(F8 ? 3 : 2) * (NT / 64) + 2];
     __shared__ uint32_t status;
     __shared__ int64_t taken;
     if (kCoop && threadIdx.x == 0) {
@@ -559,14 +660,15 @@ __global__ __launch_bounds__(NT) void adam8_kernel(StepArgs a) {
     }
     const float s = a.b.gscale ? *a.b.gscale : 1.0f;
     if (kCoop && status != 0u && d.kind == KIND_VEC && d.nparts > 1 && d.run_log2 < 0) {
-        if (d.part == 0) block_sweeps<NT>(a.b.chunks + c, d.nparts, d.blk, a, s, dqm, dqv, red);
+        if (d.part == 0)
+            block_sweeps<NT, F8>(a.b.chunks + c, d.nparts, d.blk, a, s, dqm, dqv, red);
         return;
     }
-    one_chunk<kCoop ? MODE_COOP : MODE, NT, KG>(d, c, a, s, dqm, dqv, red);
+    one_chunk<kCoop ? MODE_COOP : MODE, NT, KG, F8>(d, c, a, s, dqm, dqv, red);
 }
 
 // Workgroups of a cooperative kernel the device holds at once.
-template <int MODE, int NT, int KG>
+template <int MODE, int NT, int KG, bool F8>
 int coop_capacity() {
     static std::mutex mu;
     static int cached[64] = {0};
@@ -576,7 +678,7 @@ int coop_capacity() {
     if (cached[dev] == 0) {
         int per_cu = 0, ncu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-                &per_cu, reinterpret_cast<const void*>(adam8_kernel<MODE, NT, KG>), NT, 0) !=
+                &per_cu, reinterpret_cast<const void*>(adam8_kernel<MODE, NT, KG, F8>), NT, 0) !=
                 hipSuccess ||
             hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
@@ -585,26 +687,32 @@ int coop_capacity() {
     return cached[dev];
 }
 
-template <int NT, int KG>
-hipError_t launch_nt(const StepArgs& a, int32_t mode, int32_t max_nparts, hipStream_t s) {
+template <int NT, int KG, bool F8>
+hipError_t launch_mode(const StepArgs& a, int32_t mode, int32_t max_nparts, hipStream_t s) {
     const dim3 grid((unsigned)a.nwg), block(NT);
     if (max_nparts > 1 && mode == RS_SPLIT_COOPERATIVE &&
-        coop_ok(max_nparts, coop_capacity<MODE_COOP, NT, KG>())) {
-        hipLaunchKernelGGL((adam8_kernel<MODE_COOP, NT, KG>), grid, block, 0, s, a);
+        coop_ok(max_nparts, coop_capacity<MODE_COOP, NT, KG, F8>())) {
+        hipLaunchKernelGGL((adam8_kernel<MODE_COOP, NT, KG, F8>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     if (max_nparts > 1 && mode == RS_SPLIT_ORDERED &&
-        ordered_ok(max_nparts, coop_capacity<MODE_ORDERED, NT, KG>())) {
-        hipLaunchKernelGGL((adam8_kernel<MODE_ORDERED, NT, KG>), grid, block, 0, s, a);
+        ordered_ok(max_nparts, coop_capacity<MODE_ORDERED, NT, KG, F8>())) {
+        hipLaunchKernelGGL((adam8_kernel<MODE_ORDERED, NT, KG, F8>), grid, block, 0, s, a);
         return hipGetLastError();
     }
     if (max_nparts > 1) {
-        hipLaunchKernelGGL((adam8_kernel<MODE_PARTIAL, NT, KG>), grid, block, 0, s, a);
+        hipLaunchKernelGGL((adam8_kernel<MODE_PARTIAL, NT, KG, F8>), grid, block, 0, s, a);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
-    hipLaunchKernelGGL((adam8_kernel<MODE_MAIN, NT, KG>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((adam8_kernel<MODE_MAIN, NT, KG, F8>), grid, block, 0, s, a);
     return hipGetLastError();
+}
+
+template <int NT, int KG>
+hipError_t launch_nt(const StepArgs& a, int32_t mode, int32_t max_nparts, hipStream_t s) {
+    if (a.b.fp8) return launch_mode<NT, KG, true>(a, mode, max_nparts, s);
+    return launch_mode<NT, KG, false>(a, mode, max_nparts, s);
 }
 
 }  // namespace

@@ -49,47 +49,13 @@ struct Fp8Args {
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-// The E4M3 conversions are gfx950's OCP FP8 instructions: encoding rounds to
-// nearest even on the E4M3 grid (subnormals included), decoding is exact.
-// Saturation is explicit: a quotient beyond +-448 (possible only when s is
-// a subnormal binary32) is clamped first.
-__device__ __forceinline__ float e4m3_sat(float q) { return __builtin_amdgcn_fmed3f(q, -448.0f, 448.0f); }
-
-// Codes of q0..q3 in bytes 0..3.
-__device__ __forceinline__ uint32_t e4m3x4(float q0, float q1, float q2, float q3) {
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(q0), e4m3_sat(q1), 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(q2), e4m3_sat(q3), w, true);
-    return (uint32_t)w;
-}
-
-__device__ __forceinline__ uint32_t e4m3_code(float q) {
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(e4m3_sat(q), 0.0f, 0, false) & 0xffu;
-}
-
+// Exact decode of one E4M3 code (gfx950 conversion).
 __device__ __forceinline__ float e4m3_value(uint32_t c) { return __builtin_amdgcn_cvt_f32_fp8((int)c, 0); }
 
 // bf16 bits of (a, b), round to nearest even, a in the low half.
 __device__ __forceinline__ uint32_t bf16x2_bits(float a, float b) {
     const f32x2 v = {a, b};
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-
-// Quotient x / s of the block rule (correctly rounded), y = RN(1 / s).  The
-// correction step of ratio_fast returns +0 for x = -0; the sign is x's.
-__device__ __forceinline__ float fp8_ratio(float x, float s, float y) {
-    return __builtin_copysignf(quant_slow(s) ? x / s : ratio_fast(x, s, y), x);
-}
-
-// Code of x in a block of scale s (s >= 0; s == 0 gives code 0).
-__device__ __forceinline__ uint32_t fp8_of(float x, float s, float y) {
-    return s == 0.0f ? 0u : e4m3_code(fp8_ratio(x, s, y));
-}
-
-// Codes of four elements of one block.
-__device__ __forceinline__ uint32_t fp8x4_of(const float4& x, float s, float y) {
-    if (s == 0.0f) return 0u;
-    return e4m3x4(fp8_ratio(x.x, s, y), fp8_ratio(x.y, s, y), fp8_ratio(x.z, s, y),
-                  fp8_ratio(x.w, s, y));
 }
 
 // n zero bytes from p (p is any byte address of a 16-byte aligned buffer).

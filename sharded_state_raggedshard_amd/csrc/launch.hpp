@@ -75,6 +75,14 @@ struct StepBuffers {
     ChunkPartial* cpart;
     PartSlot* coop;
     CoopCounters* counters;
+    // FP8 output of the new parameters (nullable: no FP8 output): codes at
+    // buffer positions and one scale per global block; with it, the split
+    // reductions carry the parameters' maximum in cpart_t (two-pass) and in
+    // the .m words of coop_t (one launch), one entry per chunk
+    uint8_t* fp8;
+    float* fp8_scale;
+    float* cpart_t;
+    PartSlot* coop_t;
 };
 
 // Chunk-index ranges [lo, hi) of the chunk table; mode RS_SPLIT_*.  A

@@ -735,6 +735,10 @@ rs_status build_tables(Plan& p, std::string& err) {
     off = align256(off + p.chunks.size() * sizeof(ChunkPartial));
     p.off_coop = off;
     off = align256(off + p.chunks.size() * sizeof(PartSlot));
+    p.off_cpart_t = off;
+    off = align256(off + p.chunks.size() * sizeof(float));
+    p.off_coop_t = off;
+    off = align256(off + p.chunks.size() * sizeof(PartSlot));
     p.off_chunks8 = off;
     off = align256(off + p.chunks8.size() * sizeof(ChunkDesc));
     p.off_cpart8 = off;

@@ -52,6 +52,7 @@ struct Plan {
     // workspace layout (byte offsets)
     size_t off_tstart = 0, off_tend = 0, off_src = 0, off_dst = 0, off_gidx = 0;
     size_t off_chunks = 0, off_cpart = 0, off_coop = 0, off_l2 = 0, off_flag = 0;
+    size_t off_cpart_t = 0, off_coop_t = 0;  // the step's third value (FP8 output)
     size_t off_chunks8 = 0, off_cpart8 = 0, off_coop8 = 0;
     size_t ws_bytes = 0;
 

@@ -223,6 +223,8 @@ def test_invalid_specs_and_arguments():
     _expect(rs.RS_ESTATE, rs.rs_group_l2norm_clip, h, 0, 0, fake, rs.RS_BF16, 1.0, fake, fake,
             stream=0)
     _expect(rs.RS_ESTATE, rs.rs_adam8_step, h, 0, 0, fake, fake, fake, fake, fake, fake, stream=0)
+    _expect(rs.RS_ESTATE, rs.rs_adam8_step_fp8, h, 0, 0, fake, fake, fake, fake, fake, fake,
+            fake, fake, stream=0)
     _expect(rs.RS_ESTATE, rs.rs_bind_views, h, rs.RS_VIEW_F32_SRC, [fake], stream=0)
     _expect(rs.RS_ESTATE, rs.rs_plan_check_device, h, stream=0)
     _expect(rs.RS_ESTATE, rs.rs_plan_status_offset, h)
@@ -233,6 +235,14 @@ def test_invalid_specs_and_arguments():
     _expect(rs.RS_EINVAL, rs.rs_group_zero, h, 0, 0, fake, 9, stream=0)
     _expect(rs.RS_EINVAL, rs.rs_adam8_step, h, 0, 0, fake, fake + 8, fake, fake, fake, fake,
             stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_adam8_step_fp8, h, 0, 0, fake, fake, fake, fake, fake, fake,
+            0, fake, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_adam8_step_fp8, h, 0, 0, fake, fake, fake, fake, fake, fake,
+            fake, 0, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_adam8_step_fp8, h, 0, 0, fake, fake, fake, fake, fake, fake,
+            fake + 4, fake, stream=0)
+    _expect(rs.RS_EINVAL, rs.rs_adam8_step_fp8, h, 0, 0, fake, fake, fake, fake, fake, fake,
+            fake, fake + 2, stream=0)
     _expect(rs.RS_EINVAL, rs.rs_clip_coef, fake, -1.0, fake, stream=0)
     _expect(rs.RS_EINVAL, rs.rs_group_l2norm_clip, h, 0, 0, fake, rs.RS_BF16, 0.0, fake, fake,
             stream=0)
