@@ -34,10 +34,11 @@ workload on the host: the tensors of one layer plus the final norm, cut
 into row-block pieces, once on one thread and once on `min(16, cpus)`
 threads (the pieces dealt out by size; the oracle code is unchanged).
 
-Prints one JSON line.
+Prints one JSON line.  `--muon-only` prints only the Muon figures (a line
+with the key "muon"), for profiling the Newton-Schulz kernels on their own.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload llama8b_full]
-                    [--rank R] [--no-per-config] [--cpu-budget S]
+                    [--rank R] [--no-per-config] [--cpu-budget S] [--muon-only]
 """
 from __future__ import annotations
 
@@ -579,6 +580,8 @@ def main():
     ap.add_argument("--chunk", type=int, default=None, help="elements per workgroup in the step")
     ap.add_argument("--cpu-budget", type=float, default=16.0,
                     help="seconds of oracle work for the CPU baseline, both legs (0 = skip)")
+    ap.add_argument("--muon-only", action="store_true",
+                    help="time only the distributed-Muon cases and print their figures")
     ap.add_argument("--no-per-config", action="store_true",
                     help="skip the per-op timing of the other workloads")
     ap.add_argument("--pmc-calibration", action="store_true",
@@ -599,6 +602,9 @@ def main():
     w = synth.WORKLOADS[args.workload]()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.muon_only:
+        print(json.dumps({"muon": [muon_bench(dev, n, r) for n, r in MUON_CASES]}), flush=True)
+        return
     if args.rank is not None and not 0 <= args.rank < w.m:
         raise SystemExit(f"--rank must be in 0..{w.m - 1}")
     mode = rs.RS_SPLIT_COOPERATIVE if args.split_mode == "cooperative" else rs.RS_SPLIT_TWO_PASS

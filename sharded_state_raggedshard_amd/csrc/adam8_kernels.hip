@@ -212,9 +212,9 @@ struct VecState {
     bool wait;                   // the block's other chunks must be waited for
 };
 
-// New parameters of this lane's slice k: the hardware square root and
-// reciprocal, or correctly rounded operations where param_fast asks for them.
-template <int KG>
+// New parameters of four elements (one slice of a lane): the hardware square
+// root and reciprocal, or correctly rounded operations where param_fast asks
+// for them.
 __device__ __forceinline__ void new_params(const StepScalars& sc, const float4& th,
                                            const float* M, const float* V, float (&t)[4]) {
     const float t0[4] = {th.x, th.y, th.z, th.w};
@@ -271,7 +271,7 @@ __device__ __forceinline__ bool vec_front(const ChunkDesc& d, int64_t c, const S
 #pragma unroll
         for (int k = 0; k < KG; ++k) {
             float t[4];
-            new_params<KG>(sc, in.TH[k], st.M + 4 * k, st.V + 4 * k, t);
+            new_params(sc, in.TH[k], st.M + 4 * k, st.V + 4 * k, t);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 st.T[4 * k + j] = t[j];
@@ -369,7 +369,7 @@ __device__ __forceinline__ void vec_params(const ChunkDesc& d, const StepArgs& a
 #pragma unroll
             for (int j = 0; j < 4; ++j) t[j] = st.T[4 * k + j];
         } else {
-            new_params<KG>(sc, in.TH[k], st.M + 4 * k, st.V + 4 * k, t);
+            new_params(sc, in.TH[k], st.M + 4 * k, st.V + 4 * k, t);
         }
         st_f4(th_b + p[k], t[0], t[1], t[2], t[3]);
         if (out_b)
