@@ -34,7 +34,8 @@
  *   - Device pointers must be 16-byte aligned.
  *   - Concurrency: calls on distinct plans are independent.  Device calls on
  *     one plan share that plan's workspace scratch and must be ordered on
- *     one stream (or synchronised by the caller).
+ *     one stream (or synchronised by the caller); the one exception,
+ *     rs_muon_orthogonalize for different roots, is stated there.
  */
 #ifndef RAGGEDSHARD_H
 #define RAGGEDSHARD_H
@@ -417,9 +418,11 @@ rs_status rs_muon_gather(const rs_muon* muon, int32_t root, float* d_mom, const 
                          const rs_muon_hparams* hp, uint16_t* d_root, void* stream);
 
 /* Newton-Schulz of the matrices of `root` (RS_ALL: every root), in place in
- * the root buffer: reads U, leaves O (bf16).  Uses the workspace's buffers,
- * so calls on one Muon plan must be stream-ordered.  Errors as
- * rs_muon_gather. */
+ * the root buffer: reads U, leaves O (bf16).  Uses the workspace's buffers
+ * of those matrices only: calls for different roots touch disjoint memory
+ * and may run concurrently on different streams (one GPU standing in for
+ * several roots); calls whose roots overlap (the same root, or RS_ALL)
+ * must be stream-ordered.  Errors as rs_muon_gather. */
 rs_status rs_muon_orthogonalize(const rs_muon* muon, int32_t root, uint16_t* d_root, void* stream);
 
 /* Redistribution back and the update, for the matrices of `root` (RS_ALL:

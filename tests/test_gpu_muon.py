@@ -165,6 +165,34 @@ def test_per_root_calls_compose_and_stay_in_their_region():
 
 
 @pytest.mark.parametrize("name", list(CASES))
+def test_per_root_calls_on_streams_match_the_all_root_call(name):
+    """Per-root calls on four streams at once (each root's matrices use their
+    own workspace buffers) give the all-root call's bits."""
+    specs, L, plan, mats, mu, shapes = _setup(name)
+    log(f"muon per-root calls on streams {name}")
+    U = np.zeros(mu.root_elems, np.uint16)
+    for k, (R, C) in enumerate(shapes):
+        U[mu.offsets[k]:mu.offsets[k] + R * C] = _rand_bf16(R * C, 8, k, 1e-3)
+    whole = u16_to_dev(U)
+    rs.rs_muon_orthogonalize(mu.h, rs.RS_ALL, whole)
+    parts = u16_to_dev(U)
+    main = torch.cuda.current_stream()
+    streams = [torch.cuda.Stream() for _ in range(4)]
+    for st in streams:
+        st.wait_stream(main)
+    roots = sorted(set(mu.roots))
+    for j, r in enumerate(roots):
+        rs.rs_muon_orthogonalize(mu.h, r, parts, stream=streams[j % len(streams)])
+    for st in streams:
+        main.wait_stream(st)
+    torch.cuda.synchronize()
+    assert len(roots) > 1
+    assert np.array_equal(dev_to_u16(parts), dev_to_u16(whole))
+    mu.free()
+    plan.free()
+
+
+@pytest.mark.parametrize("name", list(CASES))
 def test_whole_step_against_oracle(name):
     """gather -> orthogonalize -> apply over all roots, two free-running steps,
     against the oracle chain (momentum exact, O within the tolerance above)."""
