@@ -216,18 +216,22 @@ def test_step_fp8_status_word_path(chunk, mode):
     plan.free()
 
 
-@pytest.mark.parametrize("name", ["llama_layer", "moe_rank0"])
+@pytest.mark.parametrize("name", ["llama_layer", "moe_rank0", "llama8b_full"])
 def test_step_fp8_full_size_matches_step_and_copy_in(name):
     """Full-size workloads (the one-layer bucket, 51.4M elements; one MoE
-    rank's shard of 90-chunk blocks), one launch as timed: the fused
-    outputs equal rs_adam8_step's and rs_pack_shard_fp8's of the new master,
-    compared on the device element by element."""
+    rank's shard of 90-chunk blocks; the 8.03e9-parameter state, positions
+    past 2^32), one launch as timed: the fused outputs equal rs_adam8_step's
+    and rs_pack_shard_fp8's of the new master, compared on the device
+    element by element."""
     if name == "llama_layer":
         w = synth.llama_layer_2048()
         bucket, rank = rs.RS_ALL, rs.RS_ALL
-    else:
+    elif name == "moe_rank0":
         w = synth.moe_bucket()
         bucket, rank = 0, 0
+    else:
+        w = synth.llama8b_full()
+        bucket, rank = rs.RS_ALL, rs.RS_ALL
     log(f"step fp8 full size {name}")
     plan = make_plan(w.specs, w.m, w.g_coll)
     total, nblk = plan.total, plan.n_blocks
@@ -246,6 +250,8 @@ def test_step_fp8_full_size_matches_step_and_copy_in(name):
         rs.rs_adam8_step(plan.h, bucket, rank, *plain, step=t)
         for a, b in zip(st, plain):
             assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), f"step {t}"
+    del plain
+    torch.cuda.empty_cache()
     views = [st[0][plan.pos[i]:plan.pos[i] + s.numel] for i, s in enumerate(w.specs)]
     rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, views)
     pc = torch.full((total,), SENT8, dtype=torch.uint8, device="cuda")
@@ -262,8 +268,11 @@ def test_step_fp8_full_size_matches_step_and_copy_in(name):
         inside[lo:lo + plan.S[bucket]] = True
         real &= inside
     assert int(real.sum()) > 0
-    assert torch.equal(codes[real], pc[real])
-    assert bool((codes[~real] == SENT8).all())
+    # elementwise (no boolean-mask gathers: those fail past 2^32 elements)
+    assert bool(((codes == pc) | ~real).all())
+    assert bool(((codes == SENT8) | real).all())
     assert torch.equal(scale.view(torch.int32), ps.view(torch.int32))
     rs.rs_plan_check_device(plan.h)
     plan.free()
+    del st, codes, scale, views, pc, ps, real
+    torch.cuda.empty_cache()
