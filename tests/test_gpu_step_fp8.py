@@ -274,5 +274,5 @@ def test_step_fp8_full_size_matches_step_and_copy_in(name):
     assert torch.equal(scale.view(torch.int32), ps.view(torch.int32))
     rs.rs_plan_check_device(plan.h)
     plan.free()
-    del st, codes, scale, views, pc, ps, real
+    del st, theta, grad, codes, scale, views, pc, ps, real
     torch.cuda.empty_cache()
