@@ -72,6 +72,26 @@ __device__ __forceinline__ void tile_of(const Ranges& r, int64_t wg, int64_t& t0
     t1 = min(r.hi[i], (tile + 1) * kCopyTile);
 }
 
+// Tensor j of the buffer-order tables with its start, end and view, loaded
+// together (j == n: none).
+struct TensorRef {
+    int j;
+    int64_t start = 0, end = 0;
+    uint64_t view = 0;
+    __device__ TensorRef(const TensorTables& tt, int j0) : j(j0) { load(tt); }
+    __device__ void load(const TensorTables& tt) {
+        if (j < tt.n) {
+            start = tt.tstart[j];
+            end = tt.tend[j];
+            view = tt.views[j];
+        }
+    }
+    __device__ void next(const TensorTables& tt) {
+        ++j;
+        load(tt);
+    }
+};
+
 // ---------------------------------------------------------------- pack
 
 __device__ __forceinline__ void zero_seg16(uint16_t* buf, int64_t s, int64_t e) {
@@ -122,18 +142,19 @@ __global__ __launch_bounds__(kCopyThreads) void pack_kernel(Ranges r, TensorTabl
                                                              uint16_t* __restrict__ buf) {
     int64_t t0, t1;
     tile_of(r, blockIdx.x, t0, t1);
-    int j = tt.gidx[t0 / kGranule];
-    while (j < tt.n && tt.tend[j] <= t0) ++j;
+    // the tile's first tensor from the granule index (one granule per tile),
+    // then its start, end and view in one dependent step
+    TensorRef t(tt, tt.gidx[t0 / kGranule]);
+    while (t.j < tt.n && t.end <= t0) t.next(tt);
     int64_t cur = t0;
     while (cur < t1) {
-        if (j < tt.n && tt.tstart[j] < t1) {
-            const int64_t ts = tt.tstart[j];
-            const int64_t s = max(cur, ts);
+        if (t.j < tt.n && t.start < t1) {
+            const int64_t s = max(cur, t.start);
             if (s > cur) zero_seg16(buf, cur, s);
-            const int64_t e = min(t1, tt.tend[j]);
-            pack_seg(buf, reinterpret_cast<const float*>(tt.views[j]), ts, s, e, tt.vec_ok != 0);
+            const int64_t e = min(t1, t.end);
+            pack_seg(buf, reinterpret_cast<const float*>(t.view), t.start, s, e, tt.vec_ok != 0);
             cur = e;
-            ++j;
+            t.next(tt);
         } else {
             zero_seg16(buf, cur, t1);
             cur = t1;
@@ -147,15 +168,15 @@ __global__ __launch_bounds__(kCopyThreads) void unpack_kernel(Ranges r, TensorTa
                                                                const uint16_t* __restrict__ buf) {
     int64_t t0, t1;
     tile_of(r, blockIdx.x, t0, t1);
-    int j = tt.gidx[t0 / kGranule];
-    while (j < tt.n && tt.tend[j] <= t0) ++j;
+    TensorRef t(tt, tt.gidx[t0 / kGranule]);
+    while (t.j < tt.n && t.end <= t0) t.next(tt);
     const int tid = threadIdx.x;
-    for (; j < tt.n && tt.tstart[j] < t1; ++j) {
-        const int64_t ts = tt.tstart[j];
-        uint16_t* dst = reinterpret_cast<uint16_t*>(tt.views[j]);
+    for (; t.j < tt.n && t.start < t1; t.next(tt)) {
+        const int64_t ts = t.start;
+        uint16_t* dst = reinterpret_cast<uint16_t*>(t.view);
         if (dst == buf + ts) continue;  // the view aliases the gathered buffer
         const int64_t s = max(t0, ts);
-        const int64_t e = min(t1, tt.tend[j]);
+        const int64_t e = min(t1, t.end);
         if (!tt.vec_ok) {
             for (int64_t p = s + tid; p < e; p += kCopyThreads) dst[p - ts] = buf[p];
             continue;

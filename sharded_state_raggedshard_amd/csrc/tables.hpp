@@ -72,7 +72,7 @@ constexpr int64_t kMaxChunk = int64_t(16) * kMaxStepThreads;  // 16 elements per
 constexpr int kMaxRunLog2 = 8;       // small-block runs: blocks of 4..256 elements
 constexpr int64_t kDefaultChunk = 8192;
 constexpr int64_t kFp8Chunk = 16384;  // FP8 copy-in: a 128 x 128 tile is one chunk
-constexpr int64_t kGranule = 65536;  // copy-kernel tensor-lookup granule
+constexpr int64_t kGranule = 8192;   // copy-kernel tensor-lookup granule (one copy tile)
 constexpr int kL2Blocks = 2048;      // max partial sums of the L2 norm
 // L2-norm scratch in 64-bit words: two tagged words per partial sum, then
 // the epoch word (a 256-byte line of its own)
