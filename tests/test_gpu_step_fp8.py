@@ -92,10 +92,11 @@ def _check_against_oracle(L, specs, pad, ref_theta, fused: Fp8Out, what=""):
         assert (np.abs(gd - ed) <= step).all(), f"{what}: codes more than one step apart"
 
 
-def _run(name, mode, chunk, steps=3, per_rank=False, warm=False, gscale=None):
+def _run(name, mode, chunk, steps=3, per_rank=False, warm=False, gscale=None, options=0):
     specs, m, g, sigma = CASES[name]()
-    L = oracle.Layout(specs, m, g)
-    plan = make_plan(specs, m, g, chunk=chunk, mode=mode)
+    L = oracle.Layout(specs, m, g, order=options & rs.RS_ORDER_MASK,
+                      align_unit=bool(options & rs.RS_ALIGN_CUT_UNIT))
+    plan = make_plan(specs, m, g, chunk=chunk, mode=mode, options=options)
     check_plan_matches(plan, L)
     hs = host_state(L, specs, seed=5, sigma=sigma, warm=warm)
     ds = DevState(hs, with_out=True)      # fused step
@@ -142,6 +143,15 @@ def test_step_fp8_per_rank_calls_warm_and_grad_scale(mode):
     log(f"step fp8 per-rank warm mode={mode}")
     _run("mixed", mode, 1024, steps=2, per_rank=True, warm=True, gscale=0.5)
     _run("multi_bucket", mode, None, steps=2, per_rank=True, warm=True)
+
+
+@pytest.mark.parametrize("options", [rs.RS_ORDER_BY_BLOCK, rs.RS_ORDER_BY_SIZE,
+                                     rs.RS_ALIGN_CUT_UNIT | rs.RS_ORDER_BY_SIZE])
+def test_step_fp8_with_planner_orders(options):
+    """Reordered plans: block ids (absmax and FP8 scales) follow buffer order."""
+    log(f"step fp8 planner options={options:#x}")
+    _run("mixed", COOP, 1024, steps=2, options=options)
+    _run("multi_bucket", COOP, None, steps=2, options=options)
 
 
 def test_step_fp8_touches_only_its_slice():
