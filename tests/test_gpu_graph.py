@@ -1,8 +1,9 @@
-"""The hot path under HIP graph capture: the entry points launch kernels
-only (no allocation, copy or memset), so a step captured once replays.
-Captured here: the allocation-free L2 norm, the clipping coefficient and
-the step with bf16 and FP8 output, on a layout with split blocks in the
-cooperative mode (cross-workgroup waits inside the graph).  Every replay
+"""The hot path under HIP graph capture: the per-step entry points launch
+kernels only (no allocation, copy or memset), so a step captured once
+replays.  Captured here: the allocation-free L2 norm, the clipping
+coefficient and the step with bf16 and FP8 output, on a layout with split
+blocks (cross-workgroup waits inside the graph in the one-launch modes, two
+launches in the two-pass mode); and a distributed-Muon step.  Every replay
 is compared bit for bit with the same sequence run eagerly on a twin of
 the state, with eager work and synchronisations between the replays."""
 import numpy as np
@@ -12,6 +13,7 @@ import torch
 import oracle
 import sharded_state_raggedshard_amd as rs
 from gpu_harness import DevState, host_state, log, make_plan
+from synth import ROWS, TensorSpec
 from test_gpu_step import CASES
 
 pytestmark = pytest.mark.gpu
@@ -40,7 +42,8 @@ class _Run:
                                                  self.codes, self.scale8, self.sumsq, self.clip)]
 
 
-@pytest.mark.parametrize("mode", [rs.RS_SPLIT_COOPERATIVE, rs.RS_SPLIT_ORDERED])
+@pytest.mark.parametrize("mode", [rs.RS_SPLIT_COOPERATIVE, rs.RS_SPLIT_ORDERED,
+                                  rs.RS_SPLIT_TWO_PASS])
 def test_captured_step_replays_like_eager_calls(mode):
     specs, m, g, sigma = CASES["mixed"]()
     log(f"graph capture mode={mode}")
@@ -70,6 +73,51 @@ def test_captured_step_replays_like_eager_calls(mode):
         other.add_(1.0)  # eager work between replays
         torch.cuda.synchronize()
     assert float(expected[0][9][0]) < 1.0  # the clip coefficient is active
-    rs.rs_plan_check_device(plan.h)
+    if mode != rs.RS_SPLIT_TWO_PASS:
+        rs.rs_plan_check_device(plan.h)
     del graph
+    plan.free()
+
+
+def test_captured_muon_step_replays_like_eager_calls():
+    """Distributed Muon (gather, Newton-Schulz, apply over every root)
+    captured once and replayed three times, against eager calls on a twin."""
+    specs = [TensorSpec("a", (136, 200), ROWS, 8), TensorSpec("b", (200, 136), ROWS, 8),
+             TensorSpec("c", (256, 512), ROWS, 32)]
+    m, g = 3, 16
+    log("graph capture muon")
+    plan = make_plan(specs, m, g)
+    mu = rs.Muon(plan, [0, 1, 2]).upload()
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    theta0 = torch.rand(plan.total, device="cuda", generator=gen) * 0.2 - 0.1
+    grad = (torch.randn(plan.total, device="cuda", generator=gen) * 1e-3).to(
+        torch.bfloat16).view(torch.int16)
+
+    def twin():
+        return {"theta": theta0.clone(), "mom": torch.zeros(plan.total, device="cuda"),
+                "root": torch.zeros(mu.root_elems, dtype=torch.int16, device="cuda")}
+
+    def sequence(st):
+        rs.rs_muon_gather(mu.h, rs.RS_ALL, st["mom"], grad, st["root"], momentum=0.95)
+        rs.rs_muon_orthogonalize(mu.h, rs.RS_ALL, st["root"])
+        rs.rs_muon_apply(mu.h, rs.RS_ALL, st["theta"], st["root"], lr=1e-3, weight_decay=0.01)
+
+    eager, graphed = twin(), twin()
+    expected = []
+    for _ in range(3):
+        sequence(eager)
+        torch.cuda.synchronize()
+        expected.append({k: v.cpu().numpy().copy() for k, v in eager.items()})
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sequence(graphed)
+    torch.cuda.synchronize()
+    assert not graphed["mom"].any()  # capture ran nothing
+    for k, exp in enumerate(expected):
+        graph.replay()
+        torch.cuda.synchronize()
+        for name, v in graphed.items():
+            assert np.array_equal(v.cpu().numpy().view(np.uint8), exp[name].view(np.uint8)), (k, name)
+    del graph
+    mu.free()
     plan.free()
