@@ -144,6 +144,54 @@ def test_orthogonalize_against_oracle(name):
     plan.free()
 
 
+def _ns5_torch_fp32(u: torch.Tensor) -> torch.Tensor:
+    """The quintic Newton-Schulz iteration (five steps, coefficients of the
+    published iteration) in binary32 torch matrix products on the device,
+    with no bf16 rounding: a reference for sizes the binary64 oracle is too
+    slow for."""
+    a, b, c = om.NS_COEFFS
+    x = u / (torch.linalg.matrix_norm(u) + 1e-7)
+    tr = x.shape[0] > x.shape[1]
+    if tr:
+        x = x.t().contiguous()
+    for _ in range(5):
+        A = x @ x.t()
+        B = b * A + c * (A @ A)
+        x = a * x + B @ x
+    return x.t().contiguous() if tr else x
+
+
+def test_orthogonalize_full_size_llama8b_layer():
+    """The 2-D matrices of one Llama-8B-shaped layer (up to 14336 x 4096, 64
+    ranks): the kernels against the binary32 torch iteration on the device,
+    within the tolerance of the bf16 storage (3% of ||O||_F), and every
+    singular value of O at most 1.25 (the quintic maps (0, 1] below it)."""
+    w = synth.llama8b_tiles(layers=1)
+    log("muon orthogonalize llama8b layer")
+    plan = make_plan(w.specs, w.m, w.g_coll)
+    mats = [i for i, s in enumerate(w.specs) if len(s.shape) == 2]
+    mu = rs.Muon(plan, mats).upload()
+    gen = torch.Generator(device="cuda").manual_seed(12)
+    root = torch.zeros(mu.root_elems, dtype=torch.int16, device="cuda")
+    shapes = [tuple(w.specs[i].shape) for i in mats]
+    for k, (R, C) in enumerate(shapes):
+        u = (torch.randn(R * C, device="cuda", generator=gen) * 1e-3).to(torch.bfloat16)
+        root[mu.offsets[k]:mu.offsets[k] + R * C] = u.view(torch.int16)
+    U = root.clone()
+    rs.rs_muon_orthogonalize(mu.h, rs.RS_ALL, root)
+    torch.cuda.synchronize()
+    for k, (R, C) in enumerate(shapes):
+        sl = slice(mu.offsets[k], mu.offsets[k] + R * C)
+        u = U[sl].view(torch.bfloat16).float().reshape(R, C)
+        o = root[sl].view(torch.bfloat16).float().reshape(R, C)
+        ref = _ns5_torch_fp32(u)
+        err = (torch.linalg.matrix_norm(o - ref) / torch.linalg.matrix_norm(ref)).item()
+        assert err < 0.03, (w.specs[mats[k]].name, err)
+        assert torch.linalg.svdvals(o).max().item() <= 1.25, w.specs[mats[k]].name
+    mu.free()
+    plan.free()
+
+
 def test_per_root_calls_compose_and_stay_in_their_region():
     specs, L, plan, mats, mu, shapes = _setup("ragged_m3")
     log("muon per-root calls")
