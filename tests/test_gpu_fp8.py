@@ -111,6 +111,34 @@ def _every_code_and_tie():
     return v
 
 
+@pytest.mark.parametrize("options", [rs.RS_ORDER_BY_BLOCK, rs.RS_ORDER_BY_SIZE,
+                                     rs.RS_ALIGN_CUT_UNIT | rs.RS_ORDER_BY_SIZE])
+def test_fp8_pack_unpack_bitexact_on_reordered_plans(options):
+    """Tensors in buffer order different from the given order: block ids
+    (scales) and positions follow the planner's order on both sides."""
+    specs, m, g = CASES["kinds"]()
+    log(f"fp8 reordered options={options:#x}")
+    L = oracle.Layout(specs, m, g, order=options & rs.RS_ORDER_MASK,
+                      align_unit=bool(options & rs.RS_ALIGN_CUT_UNIT))
+    plan = make_plan(specs, m, g, options=options)
+    check_plan_matches(plan, L)
+    hv = _views(specs, 13)
+    dv = [torch.from_numpy(v).cuda() for v in hv]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_F32_SRC, dv)
+    buf, sc, hbuf, hsc = _check_pack(L, plan, hv, dv, rs.RS_ALL, rs.RS_ALL)
+    for r in (0, m - 1):
+        _check_pack(L, plan, hv, dv, rs.RS_ALL, r)
+    outs = [torch.zeros(s.numel, dtype=torch.int16, device="cuda") for s in specs]
+    rs.rs_bind_views(plan.h, rs.RS_VIEW_BF16_DST, outs)
+    rs.rs_unpack_full_fp8(plan.h, rs.RS_ALL, buf, sc)
+    hexp = [np.zeros(s.numel, dtype=np.uint16) for s in specs]
+    L.unpack_fp8(-1, hexp, hbuf, hsc)
+    for s, o, e in zip(specs, outs, hexp):
+        assert np.array_equal(dev_to_u16(o), e), s.name
+    rs.rs_plan_check_device(plan.h)
+    plan.free()
+
+
 def test_fp8_every_code_and_tie():
     """The E4M3 rounding of the copy-in on every code and every tie, in the
     three vector paths (whole contiguous blocks, 128 x 128 tiles, runs of
