@@ -66,6 +66,28 @@ def test_step_on_ranks_without_blocks_changes_nothing(mode):
     plan.free()
 
 
+def test_fp8_output_step_on_ranks_without_blocks_writes_nothing():
+    specs, m, g = _layout()
+    L = oracle.Layout(specs, m, g)
+    plan = make_plan(specs, m, g)
+    h = host_state(L, specs, seed=5, sigma=1e-3, warm=True)
+    for b, r in _empty_ranks(plan, L):
+        log(f"empty fp8-output step bucket {b} rank {r}")
+        d = DevState(h, with_out=True)
+        codes = torch.full((L.total,), 0x5A, dtype=torch.uint8, device="cuda")
+        scale = torch.full((L.n_blocks,), -1.0, dtype=torch.float32, device="cuda")
+        rs.rs_adam8_step_fp8(plan.h, b, r, d.theta, d.grad, d.qm, d.qv, d.am, d.av, codes,
+                             scale, step=2, bf16_out=d.out)
+        got = d.host()
+        for name in ("theta", "qm", "qv", "am", "av"):
+            assert np.array_equal(getattr(got, name).view(np.uint8),
+                                  getattr(h, name).view(np.uint8)), (b, r, name)
+        assert not d.out.any()
+        assert bool((codes == 0x5A).all()) and bool((scale == -1.0).all())
+    rs.rs_plan_check_device(plan.h)
+    plan.free()
+
+
 def test_copy_ins_and_group_ops_on_ranks_without_blocks():
     specs, m, g = _layout()
     L = oracle.Layout(specs, m, g)
