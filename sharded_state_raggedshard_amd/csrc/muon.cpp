@@ -284,7 +284,7 @@ rs_status rs_muon_orthogonalize(const rs_muon* muon, int32_t root, uint16_t* d_r
     if (st != RS_OK) return st;
     bool wide = true;
     for (int32_t i = i0; i < i1; ++i)
-        wide = wide && muon->mats[size_t(i)].n % 32 == 0 && muon->mats[size_t(i)].k % 32 == 0;
+        wide = wide && muon->mats[size_t(i)].n % 64 == 0 && muon->mats[size_t(i)].k % 64 == 0;
     hipError_t e = rs::mu::launch_orthogonalize(device_tables(*muon), muon->tiles.data(), i0, i1,
                                                 c0, c1, wide, d_root,
                                                 reinterpret_cast<hipStream_t>(stream));

@@ -36,7 +36,7 @@ struct alignas(16) MuonChunk {
 constexpr int64_t kChunk = 8192;   // elements of one gather / apply chunk
 constexpr int kPrepTile = 64;      // prep kernel: 64 x 64 tiles of U
 constexpr int kGemmTile = 128;     // Newton-Schulz products: 128 x 128 output tiles,
-constexpr int kGemmTile2 = 256;    // or 256 x 256 when both dimensions are multiples of 32
+constexpr int kGemmTile2 = 256;    // or 256 x 256 when both dimensions are multiples of 64
 constexpr int64_t kRootAlign = 64; // root-buffer offsets: multiples of 64 elements
 // Newton-Schulz: the published quintic coefficients and five steps
 constexpr float kNsA = 3.4445f, kNsB = -4.7750f, kNsC = 2.0315f;
@@ -60,7 +60,7 @@ struct Tables {
 hipError_t launch_gather(const Tables& t, int64_t c0, int64_t c1, float* mom, const uint16_t* grad,
                          float mu, uint16_t* root, hipStream_t s);
 // host_tiles: a host copy of t.tiles (grid sizes).  wide: every matrix of
-// [i0, i1) has both dimensions multiples of 32, so the 256 x 256 kernel runs.
+// [i0, i1) has both dimensions multiples of 64, so the 256 x 256 kernel runs.
 hipError_t launch_orthogonalize(const Tables& t, const int64_t* host_tiles, int32_t i0, int32_t i1,
                                 int64_t c0, int64_t c1, bool wide, uint16_t* root, hipStream_t s);
 hipError_t launch_apply(const Tables& t, int64_t c0, int64_t c1, float* theta,

@@ -425,10 +425,10 @@ __global__ __launch_bounds__(GT) void ns_gemm_kernel(GemmArgs g) {
 
 // ------------------------------------------------ 256 x 256 products
 
-constexpr int T2 = 256, BK2 = 32, NSTAGE = 4;
+constexpr int T2 = 256, BK2 = 64, NSTAGE = 2;
 constexpr int GT2 = 512;               // eight waves: two per SIMD
 constexpr int kRowsPerWave2 = T2 / (GT2 / 64);
-constexpr int kStage2 = T2 * BK2;      // bf16 of one operand tile in LDS (16 KiB)
+constexpr int kStage2 = T2 * BK2;      // bf16 of one operand tile in LDS (32 KiB)
 constexpr int kOutR2 = T2 + 8;         // bf16 per row of the staged result tile
 static_assert(T2 * kOutR2 >= 2 * NSTAGE * kStage2, "the staged result tile covers the stages");
 
@@ -436,41 +436,40 @@ static_assert(T2 * kOutR2 >= 2 * NSTAGE * kStage2, "the staged result tile cover
 // memory operations of the wave are outstanding, leaving the other counters.
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-// A T2 x 32 bf16 tile (rows r0 .., k0 .. k0 + 31 of a row-major matrix) into
+// A T2 x 64 bf16 tile (rows r0 .., k0 .. k0 + 63 of a row-major matrix) into
 // LDS, straight from global memory (gfx950's 16-byte loads to LDS, no VGPR
-// staging).  LDS rows are 64 bytes; the 16-byte chunk c of row r sits at
-// chunk c ^ ((r >> 2) & 3), so the 16 lanes of a fragment read meet 16
-// different bank groups.  Wave w fills rows [32 w, 32 w + 32), sixteen rows
-// per instruction (lane l: row l / 4, physical chunk l % 4).  Rows past rmax
-// read row rmax - 1: they only feed results outside the matrix, which are
-// never stored.
+// staging).  One instruction covers eight whole 128-byte row pieces (lane l:
+// row l / 8, physical chunk l % 8): measured on this part, 128-byte pieces
+// move twice the bytes per cycle of 64-byte ones.  LDS rows are 128 bytes;
+// the 16-byte chunk c of row r sits at chunk c ^ ((r >> 1) & 7), so the 16
+// lanes of a fragment read meet 16 different bank groups.  Wave w fills rows
+// [32 w, 32 w + 32).  Rows past rmax read row rmax - 1: they only feed
+// results outside the matrix, which are never stored.
 __device__ __forceinline__ void tile_to_lds(const uint16_t* A, int64_t ld, int64_t r0,
                                             int64_t rmax, int64_t k0, uint16_t* dst) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
-    for (int j = 0; j < kRowsPerWave2 / 16; ++j) {
-        const int row = wave * kRowsPerWave2 + j * 16 + (lane >> 2);
-        const int lc = (lane & 3) ^ ((row >> 2) & 3);
+    for (int j = 0; j < kRowsPerWave2 / 8; ++j) {
+        const int row = wave * kRowsPerWave2 + j * 8 + (lane >> 3);
+        const int lc = (lane & 7) ^ ((row >> 1) & 7);
         int64_t gr = r0 + row;
         gr = gr < rmax ? gr : rmax - 1;
         __builtin_amdgcn_global_load_lds(A + gr * ld + k0 + lc * 8,
-                                         dst + (wave * kRowsPerWave2 + j * 16) * BK2, 16, 0, 0);
+                                         dst + (wave * kRowsPerWave2 + j * 8) * BK2, 16, 0, 0);
     }
 }
 
 __device__ __forceinline__ bf16x8 frag2(const uint16_t* src, int row, int lc) {
-    return *reinterpret_cast<const bf16x8*>(src + row * BK2 + ((lc ^ ((row >> 2) & 3)) << 3));
+    return *reinterpret_cast<const bf16x8*>(src + row * BK2 + ((lc ^ ((row >> 1) & 7)) << 3));
 }
 
-// One 256 x 256 tile of a product whose K is a multiple of 32.  Eight waves
+// One 256 x 256 tile of a product whose K is a multiple of 64.  Eight waves
 // (two per SIMD, so one wave's LDS reads and barrier overlap the other's
 // MFMAs), each a 128 x 64 part as 4 x 2 MFMA tiles (128 accumulators per
-// lane); both operand tiles go straight to LDS through four stages, loads
-// issued three stages ahead of the multiplications so that their latency is
-// hidden behind three stages of MFMA work.  The addend is read through its
-// transpose Rt (A itself, or X for Y), so the four consecutive rows a lane
-// holds for one column are 8 contiguous bytes.  One workgroup per compute
-// unit (132 KiB of LDS).
+// lane); both operand tiles go straight to LDS through two stages of 64
+// K-columns, the next stage's loads in flight while the current one is
+// multiplied (each stage in two halves: 12 fragment reads, then 16 MFMAs).
+// One workgroup per compute unit (132 KiB of LDS).
 __global__ __launch_bounds__(GT2) void ns_gemm256_kernel(GemmArgs g) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[T2 * kOutR2];
     const int nm = g.t.nm;
@@ -507,10 +506,10 @@ __global__ __launch_bounds__(GT2) void ns_gemm256_kernel(GemmArgs g) {
     for (int s = 0; s < NSTAGE - 1; ++s)
         if (s < KT) issue(s);
     for (int kt = 0; kt < KT; ++kt) {
-        // stage kt has landed once at most the later stages' loads (4 per
+        // stage kt has landed once at most the later stages' loads (8 per
         // stage per wave) are outstanding; the barrier then also tells every
         // wave that all are done reading the stage the next issue overwrites
-        constexpr int kPerStage = 2 * (kRowsPerWave2 / 16);
+        constexpr int kPerStage = 2 * (kRowsPerWave2 / 8);
         const int later = min(NSTAGE - 2, KT - 1 - kt);
         if (later >= 2)
             __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kPerStage));
@@ -525,27 +524,30 @@ __global__ __launch_bounds__(GT2) void ns_gemm256_kernel(GemmArgs g) {
         if (kt + NSTAGE - 1 < KT) issue(kt + NSTAGE - 1);
         const uint16_t* sp = lds + (kt % NSTAGE) * 2 * kStage2;
         const uint16_t* sq = sp + kStage2;
-        // every fragment of the stage is read up front (12 reads), then the 16
-        // MFMAs run back to back
-        bf16x8 fa[BK2 / 16][TI], fb[BK2 / 16][TJ];
+        // each half of the stage: its 12 fragments read up front, then its 16
+        // MFMAs back to back
 #pragma unroll
-        for (int kk = 0; kk < BK2 / 16; ++kk) {
-            const int lc = 2 * kk + half;
+        for (int hh = 0; hh < BK2 / 32; ++hh) {
+            bf16x8 fa[2][TI], fb[2][TJ];
 #pragma unroll
-            for (int i = 0; i < TI; ++i) fa[kk][i] = frag2(sp, wm * 128 + i * 32 + frow, lc);
+            for (int k2 = 0; k2 < 2; ++k2) {
+                const int lc = 2 * (2 * hh + k2) + half;
 #pragma unroll
-            for (int j = 0; j < TJ; ++j) fb[kk][j] = frag2(sq, wn * 64 + j * 32 + frow, lc);
+                for (int i = 0; i < TI; ++i) fa[k2][i] = frag2(sp, wm * 128 + i * 32 + frow, lc);
+#pragma unroll
+                for (int j = 0; j < TJ; ++j) fb[k2][j] = frag2(sq, wn * 64 + j * 32 + frow, lc);
+            }
+#pragma unroll
+            for (int k2 = 0; k2 < 2; ++k2)
+#pragma unroll
+                for (int i = 0; i < TI; ++i)
+#pragma unroll
+                    for (int j = 0; j < TJ; ++j)
+                        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[k2][i], fb[k2][j],
+                                                                            acc[i][j], 0, 0, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 2 * (TI + TJ), 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, 2 * TI * TJ, 0);
         }
-#pragma unroll
-        for (int kk = 0; kk < BK2 / 16; ++kk)
-#pragma unroll
-            for (int i = 0; i < TI; ++i)
-#pragma unroll
-                for (int j = 0; j < TJ; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[kk][i], fb[kk][j],
-                                                                        acc[i][j], 0, 0, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, (BK2 / 16) * (TI + TJ), 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, (BK2 / 16) * TI * TJ, 0);
     }
     __syncthreads();  // every wave is done with the stages: LDS is free
     // results bf16(alpha acc + beta R), stored straight and/or transposed as

@@ -44,8 +44,17 @@ def _ragged_specs():
             TensorSpec("d", (264, 520), ROWS, 8), TensorSpec("e", (520, 48), ROWS, 8)]
 
 
+def _wide64_specs():
+    # every dimension a multiple of 64, none of 256: the 256 x 256 product
+    # kernel on partial tiles, with odd numbers of 64-column stages (K = 192,
+    # 320, 448, 576) and a two-stage one (K = 128)
+    return [TensorSpec("p", (320, 192), ROWS, 8), TensorSpec("q", (192, 448), ROWS, 8),
+            TensorSpec("r", (576, 128), ROWS, 8), TensorSpec("s", (64, 64), ROWS, 8)]
+
+
 CASES = {
     "ragged_m3": lambda: (_ragged_specs(), 3, 16),
+    "wide64_m2": lambda: (_wide64_specs(), 2, 16),
     "llama_layer": lambda: (synth.llama_layer_2048().specs, 8, 16),
 }
 
