@@ -354,10 +354,12 @@ def per_config(dev, reps, warmup):
 
 # --------------------------------------------------------- distributed Muon
 
-def muon_tile_flops(shapes, tile=128):
-    """MFMA work the Newton-Schulz kernels do: 128 x 128 output tiles, the
-    symmetric products (A = X X^T, B = c A A + b A) on and above the
-    diagonal only; five steps."""
+def muon_tile_flops(shapes):
+    """MFMA work the Newton-Schulz kernels do: output tiles of 256 x 256 when
+    every dimension is a multiple of 64 (the 256 x 256 kernel runs), else
+    128 x 128; the symmetric products (A = X X^T, B = c A A + b A) on and
+    above the diagonal only; five steps."""
+    tile = 256 if all(R % 64 == 0 and C % 64 == 0 for R, C in shapes) else 128
     tot = 0
     for R, C in shapes:
         n, k = min(R, C), max(R, C)
