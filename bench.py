@@ -591,8 +591,8 @@ def main():
                          "kernel of known size for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no "
-              "multi-GPU path (the RCCL all-gather / reduce-scatter of the planned buffers is "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): the library has "
+              "no multi-GPU path (the RCCL all-gather / reduce-scatter of the planned buffers is "
               "not part of it); every figure is one GPU's", file=sys.stderr)
         sys.exit(2)
 
