@@ -52,9 +52,19 @@ def _wide64_specs():
             TensorSpec("r", (576, 128), ROWS, 8), TensorSpec("s", (64, 64), ROWS, 8)]
 
 
+def _mixed32_specs():
+    # a matrix whose dimensions are multiples of 32 but not of 64 sends an
+    # all-root call to the 128 x 128 kernel, while per-root calls of the other
+    # root take the 256 x 256 kernel: the per-root test then compares the two
+    # kernels bit for bit
+    return [TensorSpec("u", (96, 160), ROWS, 8), TensorSpec("p", (320, 192), ROWS, 8),
+            TensorSpec("q", (192, 448), ROWS, 8)]
+
+
 CASES = {
     "ragged_m3": lambda: (_ragged_specs(), 3, 16),
     "wide64_m2": lambda: (_wide64_specs(), 2, 16),
+    "mixed32_m2": lambda: (_mixed32_specs(), 2, 16),
     "llama_layer": lambda: (synth.llama_layer_2048().specs, 8, 16),
 }
 
