@@ -24,9 +24,11 @@
  *   - stream: a hipStream_t passed as void* (NULL = the null stream).  Every
  *     device call is asynchronous and stream-ordered; nothing synchronises
  *     the host except rs_plan_upload and rs_bind_views.
- *   - Ownership: the library owns only the host-side rs_plan.  The caller
- *     owns every device allocation (DBuffers, absmax arrays, workspace,
- *     views) and the stream.  The library never allocates device memory.
+ *   - Ownership: the library owns the host-side plans, and a Muon plan also
+ *     one stream and two events of its own (created by rs_muon_upload,
+ *     released by rs_muon_free).  The caller owns every device allocation
+ *     (DBuffers, absmax arrays, workspace, views) and the stream.  The
+ *     library never allocates device memory.
  *   - Errors: every call returns an rs_status; all argument checks happen on
  *     the host before any launch, and a failed check launches nothing.
  *     rs_last_error() returns a thread-local message for the last non-OK
@@ -405,8 +407,10 @@ rs_status rs_muon_layout(const rs_muon* muon, int32_t* roots, int64_t* offsets, 
 size_t rs_muon_device_bytes(const rs_muon* muon);
 
 /* Copies the tables into the caller's workspace (>= rs_muon_device_bytes,
- * 256-byte aligned); the Muon plan keeps the pointer.  Synchronises the
- * stream.  Errors: RS_EINVAL, RS_ENOMEM (too small), RS_EHIP. */
+ * 256-byte aligned); the Muon plan keeps the pointer.  On its first call it
+ * also creates the plan's own stream and two events on the current device
+ * (used by rs_muon_orthogonalize).  Synchronises the stream.  Errors:
+ * RS_EINVAL, RS_ENOMEM (too small), RS_EHIP. */
 rs_status rs_muon_upload(rs_muon* muon, void* d_workspace, size_t bytes, void* stream);
 
 /* Momentum and redistribution to the roots, for the matrices of `root`
@@ -422,7 +426,13 @@ rs_status rs_muon_gather(const rs_muon* muon, int32_t root, float* d_mom, const 
  * of those matrices only: calls for different roots touch disjoint memory
  * and may run concurrently on different streams (one GPU standing in for
  * several roots); calls whose roots overlap (the same root, or RS_ALL)
- * must be stream-ordered.  Errors as rs_muon_gather. */
+ * must be stream-ordered.  With two or more matrices selected whose
+ * X X^T products have fewer output tiles than two per compute unit, they run
+ * as two groups of about equal cost, the second on the plan's own stream,
+ * forked from `stream` and joined back to it with the plan's two events
+ * (event record and wait only: the call stays capturable in a HIP graph);
+ * calls on several streams at once share that stream, which orders their
+ * second groups.  Errors as rs_muon_gather. */
 rs_status rs_muon_orthogonalize(const rs_muon* muon, int32_t root, uint16_t* d_root, void* stream);
 
 /* Redistribution back and the update, for the matrices of `root` (RS_ALL:

@@ -33,6 +33,16 @@ struct rs_muon {
     size_t off_mats = 0, off_chunks = 0, off_tiles = 0, off_partials = 0, off_ns = 0, ws_bytes = 0;
     void* d_ws = nullptr;
     bool uploaded = false;
+    // a second stream for Newton-Schulz (two groups of matrices at once) and
+    // the events that fork it from and join it back to the caller's stream
+    hipStream_t aux = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
+    int32_t n_cu = 0;  // compute units of the device (at upload)
+    ~rs_muon() {
+        if (ev_join) (void)hipEventDestroy(ev_join);
+        if (ev_fork) (void)hipEventDestroy(ev_fork);
+        if (aux) (void)hipStreamDestroy(aux);
+    }
 };
 
 namespace {
@@ -251,6 +261,16 @@ rs_status rs_muon_upload(rs_muon* muon, void* d_workspace, size_t bytes, void* s
     }
     hipError_t e = hipStreamSynchronize(s);
     if (e != hipSuccess) return fail(RS_EHIP, std::string("hipStreamSynchronize: ") + hipGetErrorString(e));
+    if (!muon->aux) {
+        e = hipStreamCreateWithFlags(&muon->aux, hipStreamNonBlocking);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&muon->ev_fork, hipEventDisableTiming);
+        if (e == hipSuccess) e = hipEventCreateWithFlags(&muon->ev_join, hipEventDisableTiming);
+        int dev = 0;
+        if (e == hipSuccess) e = hipGetDevice(&dev);
+        if (e == hipSuccess)
+            e = hipDeviceGetAttribute(&muon->n_cu, hipDeviceAttributeMultiprocessorCount, dev);
+        if (e != hipSuccess) return fail(RS_EHIP, std::string("stream / event: ") + hipGetErrorString(e));
+    }
     muon->d_ws = d_workspace;
     muon->uploaded = true;
     return RS_OK;
@@ -282,12 +302,54 @@ rs_status rs_muon_orthogonalize(const rs_muon* muon, int32_t root, uint16_t* d_r
     int64_t c0, c1;
     rs_status st = select(*muon, root, i0, i1, c0, c1);
     if (st != RS_OK) return st;
-    bool wide = true;
+    const rs_muon& M = *muon;
+    // matrices [a, b): the 256 x 256 product kernel when every dimension is a
+    // multiple of 64 (both kernels give the same bits), and their chunks
+    auto run = [&](int32_t a, int32_t b, hipStream_t st) {
+        bool wide = true;
+        for (int32_t i = a; i < b; ++i)
+            wide = wide && M.mats[size_t(i)].n % 64 == 0 && M.mats[size_t(i)].k % 64 == 0;
+        const int64_t x0 = M.mats[size_t(a)].g0;
+        const int64_t x1 = M.mats[size_t(b - 1)].g0 + M.mats[size_t(b - 1)].gn;
+        return rs::mu::launch_orthogonalize(device_tables(M), M.tiles.data(), a, b, x0, x1, wide,
+                                            d_root, st);
+    };
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    // the X X^T launch's tiles (256 x 256 when every dimension is a multiple
+    // of 64, else 128 x 128): fewer than two per CU leaves CUs idle
+    bool wide_all = true;
     for (int32_t i = i0; i < i1; ++i)
-        wide = wide && muon->mats[size_t(i)].n % 64 == 0 && muon->mats[size_t(i)].k % 64 == 0;
-    hipError_t e = rs::mu::launch_orthogonalize(device_tables(*muon), muon->tiles.data(), i0, i1,
-                                                c0, c1, wide, d_root,
-                                                reinterpret_cast<hipStream_t>(stream));
+        wide_all = wide_all && M.mats[size_t(i)].n % 64 == 0 && M.mats[size_t(i)].k % 64 == 0;
+    const int64_t* gram = M.tiles.data() + (wide_all ? 4 : 1) * (int64_t)(M.mats.size() + 1);
+    const bool underfilled = gram[i1] - gram[i0] < 2 * (int64_t)M.n_cu;
+    if (i1 - i0 < 2 || !underfilled) {
+        if (i1 > i0) e = run(i0, i1, s);
+    } else {
+        // two groups of about equal Newton-Schulz cost (matrices stay in root
+        // order), the second on the plan's own stream: each group's launches
+        // then fill the CUs that the other's last round of tiles leaves idle
+        // (on a full device the two only compete, so launches of two or more
+        // tiles per CU stay on one stream).  The groups touch disjoint
+        // workspace and root-buffer regions.
+        double tot = 0.0, acc = 0.0, best = 0.0;
+        for (int32_t i = i0; i < i1; ++i) tot += ns_cost(M.mats[size_t(i)].R, M.mats[size_t(i)].C);
+        int32_t im = i0 + 1;
+        for (int32_t i = i0 + 1; i < i1; ++i) {
+            acc += ns_cost(M.mats[size_t(i - 1)].R, M.mats[size_t(i - 1)].C);
+            const double d = std::fabs(acc - (tot - acc));
+            if (i == i0 + 1 || d < best) {
+                best = d;
+                im = i;
+            }
+        }
+        e = hipEventRecord(M.ev_fork, s);
+        if (e == hipSuccess) e = hipStreamWaitEvent(M.aux, M.ev_fork, 0);
+        if (e == hipSuccess) e = run(im, i1, M.aux);
+        if (e == hipSuccess) e = run(i0, im, s);
+        if (e == hipSuccess) e = hipEventRecord(M.ev_join, M.aux);
+        if (e == hipSuccess) e = hipStreamWaitEvent(s, M.ev_join, 0);
+    }
     if (e != hipSuccess)
         return fail(RS_EHIP, std::string("Newton-Schulz launch: ") + hipGetErrorString(e));
     return RS_OK;
