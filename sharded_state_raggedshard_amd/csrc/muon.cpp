@@ -345,10 +345,15 @@ rs_status rs_muon_orthogonalize(const rs_muon* muon, int32_t root, uint16_t* d_r
         }
         e = hipEventRecord(M.ev_fork, s);
         if (e == hipSuccess) e = hipStreamWaitEvent(M.aux, M.ev_fork, 0);
-        if (e == hipSuccess) e = run(im, i1, M.aux);
-        if (e == hipSuccess) e = run(i0, im, s);
-        if (e == hipSuccess) e = hipEventRecord(M.ev_join, M.aux);
-        if (e == hipSuccess) e = hipStreamWaitEvent(s, M.ev_join, 0);
+        if (e == hipSuccess) {
+            e = run(im, i1, M.aux);
+            if (e == hipSuccess) e = run(i0, im, s);
+            // joined even after a failed launch: the caller's stream never
+            // runs ahead of work queued on the plan's stream
+            hipError_t ej = hipEventRecord(M.ev_join, M.aux);
+            if (ej == hipSuccess) ej = hipStreamWaitEvent(s, M.ev_join, 0);
+            if (e == hipSuccess) e = ej;
+        }
     }
     if (e != hipSuccess)
         return fail(RS_EHIP, std::string("Newton-Schulz launch: ") + hipGetErrorString(e));
