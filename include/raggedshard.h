@@ -403,7 +403,8 @@ rs_status rs_muon_layout(const rs_muon* muon, int32_t* roots, int64_t* offsets, 
                          int64_t* root_elems);
 
 /* Device bytes of the Muon workspace: tables, per-chunk partial sums and
- * the Newton-Schulz buffers (X, two Y, A, B per matrix, bf16). */
+ * per-matrix norms, and the Newton-Schulz buffers (X, two Y, A, B per
+ * matrix, bf16). */
 size_t rs_muon_device_bytes(const rs_muon* muon);
 
 /* Copies the tables into the caller's workspace (>= rs_muon_device_bytes,

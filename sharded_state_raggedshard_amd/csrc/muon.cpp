@@ -66,6 +66,7 @@ rs::mu::Tables device_tables(const rs_muon& M) {
     t.chunks = reinterpret_cast<const rs::mu::MuonChunk*>(w + M.off_chunks);
     t.tiles = reinterpret_cast<const int64_t*>(w + M.off_tiles);
     t.partials = reinterpret_cast<double*>(w + M.off_partials);
+    t.norms = t.partials + M.chunks.size();
     t.ws = reinterpret_cast<uint16_t*>(w + M.off_ns);
     t.nm = (int32_t)M.mats.size();
     return t;
@@ -200,8 +201,8 @@ rs_status rs_muon_plan(const rs_plan* plan, const int32_t* tensors, int32_t n, r
         o = align256(o + M->chunks.size() * sizeof(MuonChunk));
         M->off_tiles = o;
         o = align256(o + M->tiles.size() * sizeof(int64_t));
-        M->off_partials = o;
-        o = align256(o + M->chunks.size() * sizeof(double));
+        M->off_partials = o;  // per-chunk sums, then one norm per matrix
+        o = align256(o + (M->chunks.size() + M->mats.size()) * sizeof(double));
         M->off_ns = o;
         o = align256(o + size_t(ns) * 2);
         M->ws_bytes = o;

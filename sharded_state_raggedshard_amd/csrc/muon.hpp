@@ -52,6 +52,7 @@ struct Tables {
     // three products in 128 x 128 tiles; the three products in 256 x 256 tiles
     const int64_t* tiles;
     double* partials;      // one sum of squares per chunk
+    double* norms;         // per matrix: sqrt(sum of its chunk sums) + 1e-7
     uint16_t* ws;          // Newton-Schulz buffers
     int32_t nm;
 };

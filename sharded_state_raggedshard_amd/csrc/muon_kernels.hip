@@ -104,8 +104,8 @@ __global__ __launch_bounds__(kVT) void gather_kernel(Tables t, int64_t c0, float
 
 // ----------------------------------------------------------------- norm
 
-// Sum of squares of one chunk of U (binary64), the per-matrix total taken
-// by the prepare kernel in a fixed order.
+// Sum of squares of one chunk of U (binary64); the scale kernel adds a
+// matrix's chunk sums in a fixed order.
 __global__ __launch_bounds__(kVT) void norm_kernel(Tables t, int64_t c0,
                                                    const uint16_t* __restrict__ root) {
     __shared__ double red[kVT / 64];
@@ -130,27 +130,32 @@ __global__ __launch_bounds__(kVT) void norm_kernel(Tables t, int64_t c0,
     if (threadIdx.x == 0) t.partials[c0 + blockIdx.x] = s;
 }
 
+// Each matrix's scale s = sqrt(sum of its chunk sums) + 1e-7, once per
+// matrix (one workgroup each), for the prepare kernel's tiles.
+__global__ __launch_bounds__(256) void scale_kernel(Tables t, int32_t i0) {
+    __shared__ double red[4];
+    const int i = i0 + (int)blockIdx.x;
+    const MuonMat& m = t.mats[i];
+    double part = 0.0;
+    for (int64_t q = threadIdx.x; q < m.gn; q += 256) part += t.partials[m.g0 + q];
+    const double tot = wg_sum<256>(part, red);
+    if (threadIdx.x == 0) t.norms[i] = sqrt(tot) + kNsEps;
+}
+
 // ------------------------------------------------------------- prepare
 
 // X0 = bf16(U / s) (U's transpose when R > C) and Y0 = X0^T, one 64 x 64
-// tile of U per workgroup; s = sqrt(sum of the matrix's chunk sums) + 1e-7.
+// tile of U per workgroup; s from the scale kernel.
 // The quotient is the binary64 one, rounded to binary32 and then to bf16.
 __global__ __launch_bounds__(256) void prep_kernel(Tables t, int32_t i0, int32_t i1,
                                                    const uint16_t* __restrict__ root) {
     constexpr int T = kPrepTile;
-    __shared__ double red[4];
-    __shared__ double s_sh;
     __shared__ uint16_t tileT[T][T + 8];
     const int64_t* pre = t.tiles;
     const int64_t tg = pre[i0] + blockIdx.x;
     const int i = find_mat(pre, i0, i1, tg);
     const MuonMat& m = t.mats[i];
-    double part = 0.0;
-    for (int64_t q = threadIdx.x; q < m.gn; q += 256) part += t.partials[m.g0 + q];
-    const double tot = wg_sum<256>(part, red);
-    if (threadIdx.x == 0) s_sh = sqrt(tot) + kNsEps;
-    __syncthreads();
-    const double s = s_sh;
+    const double s = t.norms[i];
     const int64_t local = tg - pre[i];
     const int64_t tcols = (m.C + T - 1) / T;
     const int64_t r0 = (local / tcols) * T, cc0 = (local % tcols) * T;
@@ -661,6 +666,9 @@ hipError_t launch_orthogonalize(const Tables& t, const int64_t* host_tiles, int3
     };
     hipLaunchKernelGGL(norm_kernel, dim3((unsigned)(c1 - c0)), dim3(kVT), 0, s, t, c0, root);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(scale_kernel, dim3((unsigned)(i1 - i0)), dim3(256), 0, s, t, i0);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(prep_kernel, dim3((unsigned)count(0)), dim3(256), 0, s, t, i0, i1, root);
     e = hipGetLastError();
